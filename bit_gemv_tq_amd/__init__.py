@@ -1,0 +1,214 @@
+"""Python binding of libtq, the gfx950 ternary GEMV library (include/tq.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libtq.so``.  PyTorch provides device memory and the current
+stream; outputs that are not passed in are allocated with ``torch.empty`` on
+the input's device.  There is no CPU fallback: importing this package fails
+if ``libtq.so`` has not been built (``python bit_gemv_tq_amd/build.py``),
+and every call raises ``TQError`` on a non-OK status.
+
+Conventions (weights, packing, activation quantization and rescale) are the
+ones documented in include/tq.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtq.so")
+
+TQ_BF16 = 0
+TQ_F32 = 1
+TQ_MAX_K = 131072
+TQ_MAX_M = 64
+
+STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN",
+          4: "TQ_ERR_DTYPE", 5: "TQ_ERR_DEVICE", 6: "TQ_ERR_LAUNCH"}
+
+EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
+           "tq_gate_up_relu2", "tq_status_string")
+
+
+class TQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        text = lib.tq_status_string(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({text})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first with "
+            "`python bit_gemv_tq_amd/build.py` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    sigs = {
+        "tq_pack": [p, i64, i64, p, p],
+        "tq_act_quant": [p, i32, i64, i64, p, p, p],
+        "tq_gemv": [p, f32, p, p, i64, i64, p, p, p],
+        "tq_gemm_small": [p, f32, p, p, i64, i64, i64, p, p, p],
+        "tq_gate_up_relu2": [p, f32, p, f32, p, p, i64, i64, i64, p, p, p, p],
+    }
+    for name, args in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.tq_status_string.argtypes = [ctypes.c_int]
+    L.tq_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _check(fn, status):
+    if status != 0:
+        raise TQError(fn, status)
+
+
+def _out(t, name, shape, dtype, device):
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, name, dtype, device)
+    if t.numel() != math.prod(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, need {tuple(shape)}")
+    return t
+
+
+# --------------------------------------------------------------------------
+# the five calls
+# --------------------------------------------------------------------------
+def tq_pack(w, packed=None, stream=None):
+    """int8 ternary weights [N, K] -> packed uint8 [N/4, K]."""
+    torch = _torch()
+    _need(w, "w", torch.int8)
+    N, K = w.shape
+    packed = _out(packed, "packed", (N // 4, K), torch.uint8, w.device)
+    _check("tq_pack", lib.tq_pack(_ptr(w), N, K, _ptr(packed), _stream(stream)))
+    return packed
+
+
+def tq_act_quant(x, xq=None, x_scale=None, stream=None):
+    """Per-row absmax int8 quantization of bf16 or fp32 x [M, K] (or [K]).
+    Returns (xq int8 [M, K], x_scale fp32 [M])."""
+    torch = _torch()
+    if x.dtype == torch.bfloat16:
+        xt = TQ_BF16
+    elif x.dtype == torch.float32:
+        xt = TQ_F32
+    else:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    _need(x, "x", x.dtype)
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    M, K = x2.shape
+    xq = _out(xq, "xq", (M, K), torch.int8, x.device)
+    x_scale = _out(x_scale, "x_scale", (M,), torch.float32, x.device)
+    _check("tq_act_quant", lib.tq_act_quant(_ptr(x2), xt, M, K, _ptr(xq),
+                                            _ptr(x_scale), _stream(stream)))
+    return xq, x_scale
+
+
+def tq_gemv(packed, w_scale, xq, x_scale, y=None, acc=None, stream=None):
+    """y[n] = (float)sum_k w[n,k] q[k] * (w_scale * x_scale[0]) at M = 1."""
+    torch = _torch()
+    _need(packed, "packed", torch.uint8)
+    dev = packed.device
+    _need(xq, "xq", torch.int8, dev)
+    _need(x_scale, "x_scale", torch.float32, dev)
+    N, K = packed.shape[0] * 4, packed.shape[1]
+    if xq.numel() != K:
+        raise ValueError(f"xq has {xq.numel()} elements, need K={K}")
+    y = _out(y, "y", (N,), torch.float32, dev)
+    if acc is not None:
+        acc = _out(acc, "acc", (N,), torch.int32, dev)
+    _check("tq_gemv", lib.tq_gemv(_ptr(packed), float(w_scale), _ptr(xq),
+                                  _ptr(x_scale), N, K, _ptr(y), _ptr(acc),
+                                  _stream(stream)))
+    return y
+
+
+def tq_gemm_small(packed, w_scale, xq, x_scale, y=None, acc=None, stream=None):
+    """y[m,n] for a small batch xq [M, K] (M <= 64) on the matrix cores."""
+    torch = _torch()
+    _need(packed, "packed", torch.uint8)
+    dev = packed.device
+    _need(xq, "xq", torch.int8, dev)
+    _need(x_scale, "x_scale", torch.float32, dev)
+    N, K = packed.shape[0] * 4, packed.shape[1]
+    xq2 = xq.reshape(1, -1) if xq.dim() == 1 else xq
+    M = xq2.shape[0]
+    if xq2.shape[1] != K:
+        raise ValueError(f"xq has K={xq2.shape[1]}, packed has K={K}")
+    y = _out(y, "y", (M, N), torch.float32, dev)
+    if acc is not None:
+        acc = _out(acc, "acc", (M, N), torch.int32, dev)
+    _check("tq_gemm_small", lib.tq_gemm_small(
+        _ptr(packed), float(w_scale), _ptr(xq2), _ptr(x_scale), M, N, K,
+        _ptr(y), _ptr(acc), _stream(stream)))
+    return y
+
+
+def tq_gate_up_relu2(packed_gate, s_gate, packed_up, s_up, xq, x_scale,
+                     h=None, acc_gate=None, acc_up=None, stream=None):
+    """h = relu(g)^2 * u with g, u the gate and up projections of xq [M, K]."""
+    torch = _torch()
+    _need(packed_gate, "packed_gate", torch.uint8)
+    dev = packed_gate.device
+    _need(packed_up, "packed_up", torch.uint8, dev)
+    if packed_up.shape != packed_gate.shape:
+        raise ValueError("packed_gate and packed_up shapes differ")
+    _need(xq, "xq", torch.int8, dev)
+    _need(x_scale, "x_scale", torch.float32, dev)
+    N, K = packed_gate.shape[0] * 4, packed_gate.shape[1]
+    xq2 = xq.reshape(1, -1) if xq.dim() == 1 else xq
+    M = xq2.shape[0]
+    if xq2.shape[1] != K:
+        raise ValueError(f"xq has K={xq2.shape[1]}, packed has K={K}")
+    h = _out(h, "h", (M, N), torch.float32, dev)
+    if acc_gate is not None:
+        acc_gate = _out(acc_gate, "acc_gate", (M, N), torch.int32, dev)
+    if acc_up is not None:
+        acc_up = _out(acc_up, "acc_up", (M, N), torch.int32, dev)
+    _check("tq_gate_up_relu2", lib.tq_gate_up_relu2(
+        _ptr(packed_gate), float(s_gate), _ptr(packed_up), float(s_up),
+        _ptr(xq2), _ptr(x_scale), M, N, K, _ptr(h), _ptr(acc_gate),
+        _ptr(acc_up), _stream(stream)))
+    return h

@@ -1,0 +1,120 @@
+// tq_act_quant.hip -- tq_act_quant: per-token absmax int8 quantization.
+//
+// Per row m: a = max|x|, a' = max(a, 1e-5), inv = 127/a' (fp32, correctly
+// rounded), q = clamp(rne(x*inv), -127, 127), s_x = a'/127.  The pages do
+// not describe activation quantization; this is the library's convention
+// (one correctly rounded divide per row, round half to even, symmetric
+// clamp), applied identically wherever an fp32 value decides an int8 code.
+#include "tq_device.h"
+#include "tq_host.h"
+
+namespace tq {
+namespace {
+
+constexpr int kAqThreads = 512;
+
+// 16 consecutive activations of one row, widened exactly to fp32.
+template <bool kBf16>
+__device__ __forceinline__ void load16(const void *x, int64_t piece,
+                                       float (&v)[16]) {
+  if constexpr (kBf16) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(x) + 2 * piece;
+    const uint4 h[2] = {p[0], p[1]};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t d[4] = {h[i].x, h[i].y, h[i].z, h[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(x) + 4 * piece;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = p[i];
+      v[4 * i] = f.x;
+      v[4 * i + 1] = f.y;
+      v[4 * i + 2] = f.z;
+      v[4 * i + 3] = f.w;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t quant4(const float *v, float inv) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r = __builtin_rintf(v[i] * inv);  // v_rndne_f32: ties to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    out |= ((uint32_t)(int)r & 0xffu) << (8 * i);
+  }
+  return out;
+}
+
+// One block per activation row.
+template <bool kBf16>
+__global__ __launch_bounds__(kAqThreads) void act_quant_kernel(
+    const void *__restrict__ x, int64_t K, int8_t *__restrict__ q,
+    float *__restrict__ s_x) {
+  __shared__ float wave_max_lds[kAqThreads / kWave];
+  const int64_t m = blockIdx.x;
+  const int64_t kp = K / 16;
+  const size_t elem = kBf16 ? 2 : 4;
+  const void *xr = reinterpret_cast<const char *>(x) + (size_t)(m * K) * elem;
+
+  float a = 0.0f;
+  for (int64_t p = threadIdx.x; p < kp; p += kAqThreads) {
+    float v[16];
+    load16<kBf16>(xr, p, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+  }
+  a = wave_max(a);
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) wave_max_lds[wave] = a;
+  __syncthreads();
+  a = wave_max_lds[0];
+#pragma unroll
+  for (int w = 1; w < kAqThreads / kWave; ++w) a = fmaxf(a, wave_max_lds[w]);
+
+  const float ap = a > 1e-5f ? a : 1e-5f;
+  const float inv = 127.0f / ap;  // correctly rounded fp32 division
+
+  uint4 *qr = reinterpret_cast<uint4 *>(q + m * K);
+  for (int64_t p = threadIdx.x; p < kp; p += kAqThreads) {
+    float v[16];
+    load16<kBf16>(xr, p, v);
+    uint4 o;
+    o.x = quant4(v + 0, inv);
+    o.y = quant4(v + 4, inv);
+    o.z = quant4(v + 8, inv);
+    o.w = quant4(v + 12, inv);
+    qr[p] = o;
+  }
+  if (threadIdx.x == 0) s_x[m] = ap / 127.0f;
+}
+
+}  // namespace
+}  // namespace tq
+
+extern "C" tq_status tq_act_quant(const void *x, tq_dtype xt, int64_t M,
+                                  int64_t K, int8_t *xq, float *x_scale,
+                                  hipStream_t stream) {
+  using namespace tq;
+  if (xt != TQ_BF16 && xt != TQ_F32) return TQ_ERR_DTYPE;
+  if (check_m(M) != TQ_OK || K < 0 || K % 16 != 0 || K > TQ_MAX_K)
+    return TQ_ERR_SHAPE;
+  if (M == 0) return TQ_OK;
+  if (!x_scale || (K > 0 && (!x || !xq))) return TQ_ERR_NULL;
+  if (!aligned(x_scale, 4) || !aligned(x, 16) || !aligned(xq, 16))
+    return TQ_ERR_ALIGN;
+  DeviceInfo dev;
+  if (tq_status s = current_device(&dev)) return s;
+  if (xt == TQ_BF16)
+    return launch(act_quant_kernel<true>, dim3((unsigned)M), dim3(kAqThreads),
+                  0, stream, x, K, xq, x_scale);
+  return launch(act_quant_kernel<false>, dim3((unsigned)M), dim3(kAqThreads),
+                0, stream, x, K, xq, x_scale);
+}

@@ -1,0 +1,115 @@
+// tq_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Packed ternary layout (see include/tq.h): byte [i,k] of a [N/4,K] array
+// holds the code w+1 of row j*(N/4)+i in bits 2j..2j+1.  A dword of a packed
+// row therefore carries 4 consecutive k of 4 rows ("planes"); one 16-byte
+// load carries 16 k of 4 rows = 64 weights.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- loads
+// 16-byte streaming load of weights: read once, so hint non-temporal.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const uint4 *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// ---------------------------------------------------------------- decode
+// Offset codes c = w + 1 in {0,1,2}.  For one dword d of a packed row:
+//   plane 0: d & 0x03030303         -> c0          (bytes 0..2)
+//   plane 1: d & 0x0C0C0C0C         -> 4*c1        (bytes 0..8)
+//   plane 2: d & 0x30303030         -> 16*c2       (bytes 0..32)
+//   plane 3: (d >> 2) & 0x30303030  -> 16*c3       (bytes 0..32)
+// Every byte stays a non-negative int8, so v_dot4_i32_i8 with the int8
+// activations gives 1x, 4x, 16x, 16x the plane sums sum(c*q); the scale is
+// removed exactly by an arithmetic shift after the reduction, and
+// sum(w*q) = sum(c*q) - sum(q).
+__device__ __forceinline__ void dot_planes(uint32_t d, int x, int &a0, int &a1,
+                                           int &a2, int &a3) {
+  a0 = __builtin_amdgcn_sdot4((int)(d & 0x03030303u), x, a0, false);
+  a1 = __builtin_amdgcn_sdot4((int)(d & 0x0C0C0C0Cu), x, a1, false);
+  a2 = __builtin_amdgcn_sdot4((int)(d & 0x30303030u), x, a2, false);
+  a3 = __builtin_amdgcn_sdot4((int)((d >> 2) & 0x30303030u), x, a3, false);
+}
+
+__device__ __forceinline__ void dot_planes16(const uint4 &w, const uint4 &x,
+                                             int (&a)[4]) {
+  dot_planes(w.x, (int)x.x, a[0], a[1], a[2], a[3]);
+  dot_planes(w.y, (int)x.y, a[0], a[1], a[2], a[3]);
+  dot_planes(w.z, (int)x.z, a[0], a[1], a[2], a[3]);
+  dot_planes(w.w, (int)x.w, a[0], a[1], a[2], a[3]);
+}
+
+// Undo the per-plane scale and the code offset: exact int32.
+__device__ __forceinline__ int plane_value(int j, int scaled, int sumq) {
+  const int sh = j == 0 ? 0 : (j == 1 ? 2 : 4);
+  return (scaled >> sh) - sumq;
+}
+
+// Sum of the 4 int8 lanes of each dword of a 16-byte piece.
+__device__ __forceinline__ int sum_bytes16(const uint4 &v, int acc) {
+  acc = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, acc, false);
+  acc = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, acc, false);
+  return acc;
+}
+
+// ---------------------------------------------------------------- DPP
+// DPP controls (GCN/CDNA encoding).
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114,
+              kRowShr8 = 0x118, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ int dpp_i32(int v) {
+  // Lanes whose source is outside the row (or whose row is masked off)
+  // receive 0, so "v + dpp(v)" leaves them unchanged.
+  return __builtin_amdgcn_update_dpp(0, v, Ctrl, RowMask, 0xf, false);
+}
+
+// Sum over aligned groups of G lanes (G = 16, 32 or 64).  The total lands in
+// the LAST lane of each group (lane G-1 mod G); other lanes hold partials.
+template <int G>
+__device__ __forceinline__ int group_sum_to_last(int v) {
+  static_assert(G == 16 || G == 32 || G == 64, "group size");
+  v += dpp_i32<kRowShr1>(v);
+  v += dpp_i32<kRowShr2>(v);
+  v += dpp_i32<kRowShr4>(v);
+  v += dpp_i32<kRowShr8>(v);
+  if constexpr (G >= 32) v += dpp_i32<kRowBcast15, 0xa>(v);
+  if constexpr (G >= 64) v += dpp_i32<kRowBcast31, 0xc>(v);
+  return v;
+}
+
+// Float max over the whole wave, result valid in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1)
+    v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- epilogue
+// y = (float)acc * (s_w * s_x): two fp32 roundings, in this order.
+__device__ __forceinline__ float rescale(int acc, float c) {
+  return (float)acc * c;
+}
+
+__device__ __forceinline__ float relu2_gate(float g, float u) {
+  const float r = g > 0.0f ? g : 0.0f;
+  return (r * r) * u;
+}
+
+}  // namespace tq

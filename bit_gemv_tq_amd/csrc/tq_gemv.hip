@@ -1,0 +1,235 @@
+// tq_gemv.hip -- the ternary matrix-vector product at M = 1 (tq_gemv) and
+// the fused gate/up + squared-ReLU projection at M = 1 (tq_gate_up_relu2).
+//
+// Page "the full arc: how the 1bit.systems ternary stack got from broken to
+// 76.7 tok/s", TL;DR: a hand-tuned ternary GEMV running close to the memory-
+// bandwidth peak is the decode hot loop.  Page "BitNet" (news digest), first
+// item: with weights in {-1,0,1} every product is an add, a subtract or a
+// skip.  Page "Feature request: BitNet 1.58-bit ternary inference on ROCm
+// (gfx1151)", section "Architecture": the MLP gate is relu_squared.
+//
+// gfx950 design (the pages' own kernel targets a wave32 iGPU and is not
+// followed): the decode GEMV is bound by HBM, so the kernel streams the
+// packed weights once with coalesced 16-byte non-temporal loads, keeps the
+// int8 activation row in LDS (staged once per block), turns each 16-byte
+// piece into 16 v_dot4_i32_i8 on offset codes (see tq_device.h: mask, no
+// multiply per weight), and reduces each row's partial sums across its lane
+// group with DPP.  A lane group of LPR lanes (16, 32 or 64) owns ROWS packed
+// rows at a time (4*ROWS outputs) and walks K in strides of 16*LPR bytes,
+// UNR pieces per lane in flight.
+#include "tq_device.h"
+#include "tq_host.h"
+
+namespace tq {
+namespace {
+
+constexpr int kGemvThreads = 256;
+
+struct GemvArgs {
+  const uint8_t *p0;   // packed [N/4,K] (gate when kGate)
+  const uint8_t *p1;   // packed up (kGate only)
+  float s0, s1;        // weight scales
+  const int8_t *xq;    // [K]
+  const float *x_scale;
+  int n4;              // N/4
+  int kp;              // K/16
+  float *y;            // [N] (h when kGate)
+  int32_t *acc0;       // optional [N]
+  int32_t *acc1;       // optional [N] (kGate only)
+};
+
+template <int LPR, int ROWS, int UNR, bool kGate>
+__global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(GemvArgs g) {
+  constexpr int NM = kGate ? 2 : 1;      // weight streams
+  constexpr int G = kGemvThreads / LPR;  // lane groups per block
+  extern __shared__ uint4 x_lds[];       // K/16 pieces of int8 activations
+  __shared__ int sumq_lds[kGemvThreads / kWave];
+
+  const int kp = g.kp;
+  // Stage x once per block and form sum(q) for the code offset.
+  int sq = 0;
+  const uint4 *xg = reinterpret_cast<const uint4 *>(g.xq);
+  for (int p = threadIdx.x; p < kp; p += kGemvThreads) {
+    const uint4 v = xg[p];
+    x_lds[p] = v;
+    sq = sum_bytes16(v, sq);
+  }
+  sq = wave_sum(sq);
+  if ((threadIdx.x & (kWave - 1)) == 0) sumq_lds[threadIdx.x / kWave] = sq;
+  __syncthreads();
+  int sumq = 0;
+#pragma unroll
+  for (int w = 0; w < kGemvThreads / kWave; ++w) sumq += sumq_lds[w];
+
+  const float sx = g.x_scale[0];
+  const float c0 = g.s0 * sx;
+  const float c1 = g.s1 * sx;
+
+  const int lane = threadIdx.x % LPR;
+  const int group = threadIdx.x / LPR;
+  const int stride = gridDim.x * G * ROWS;
+  const uint4 *P[NM];
+  P[0] = reinterpret_cast<const uint4 *>(g.p0);
+  if constexpr (kGate) P[NM - 1] = reinterpret_cast<const uint4 *>(g.p1);
+
+  for (int r0 = (blockIdx.x * G + group) * ROWS; r0 < g.n4; r0 += stride) {
+    int a[NM][ROWS][4];
+    const uint4 *row[NM][ROWS];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        a[m][r][0] = a[m][r][1] = a[m][r][2] = a[m][r][3] = 0;
+        const int rr = min(r0 + r, g.n4 - 1);  // rows past the end: reread
+        row[m][r] = P[m] + (size_t)rr * kp;
+      }
+
+    for (int p0 = lane; p0 < kp; p0 += LPR * UNR) {
+      uint4 w[NM][ROWS][UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int p = p0 + u * LPR;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int r = 0; r < ROWS; ++r)
+            w[m][r][u] = p < kp ? load_stream16(row[m][r] + p)
+                                : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int p = min(p0 + u * LPR, kp - 1);  // w is zero past the end
+        const uint4 xv = x_lds[p];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int r = 0; r < ROWS; ++r) dot_planes16(w[m][r][u], xv, a[m][r]);
+      }
+    }
+
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[m][r][j] = group_sum_to_last<LPR>(a[m][r][j]);
+
+    if (lane == LPR - 1) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const int i = r0 + r;
+        if (i >= g.n4) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const size_t n = (size_t)j * g.n4 + i;
+          const int v0 = plane_value(j, a[0][r][j], sumq);
+          if (g.acc0) g.acc0[n] = v0;
+          if constexpr (kGate) {
+            const int v1 = plane_value(j, a[NM - 1][r][j], sumq);
+            if (g.acc1) g.acc1[n] = v1;
+            g.y[n] = relu2_gate(rescale(v0, c0), rescale(v1, c1));
+          } else {
+            g.y[n] = rescale(v0, c0);
+          }
+        }
+      }
+    }
+  }
+}
+
+struct GemvPlan {
+  int lpr;
+  int rows;
+  int unr;
+  int blocks;
+};
+
+GemvPlan plan_gemv(int64_t n4, int64_t kp, int num_cus, int nm) {
+  GemvPlan pl;
+  // Widest lane group that divides the row into whole 16-byte pieces per
+  // lane; rows of an odd number of pieces take masked tails.
+  if (kp % 64 == 0) pl.lpr = 64;
+  else if (kp % 32 == 0) pl.lpr = 32;
+  else if (kp % 16 == 0) pl.lpr = 16;
+  else pl.lpr = kp >= 256 ? 64 : 16;
+  pl.rows = nm == 1 ? 2 : 1;
+  pl.unr = 4;
+  const int64_t groups = kGemvThreads / pl.lpr;
+  const int64_t batches = (n4 + pl.rows - 1) / pl.rows;
+  // Residency: LDS holds K bytes per block; aim for <= 8 blocks per CU.
+  const int64_t k_bytes = kp * 16;
+  int64_t per_cu = k_bytes > 0 ? (160 * 1024) / (k_bytes + 64) : 8;
+  if (per_cu > 8) per_cu = 8;
+  if (per_cu < 1) per_cu = 1;
+  const int64_t cap = (int64_t)num_cus * per_cu;
+  const int64_t iters = (batches + groups * cap - 1) / (groups * cap);
+  int64_t blocks = (batches + groups * iters - 1) / (groups * iters);
+  if (blocks < 1) blocks = 1;
+  pl.blocks = (int)blocks;
+  return pl;
+}
+
+template <bool kGate>
+tq_status launch_gemv(const GemvPlan &pl, const GemvArgs &a, size_t lds,
+                      hipStream_t s) {
+  const dim3 grid(pl.blocks), block(kGemvThreads);
+#define TQ_GEMV_CASE(L, R, U)                                              \
+  if (pl.lpr == L && pl.rows == R && pl.unr == U) {                        \
+    auto k = gemv_m1_kernel<L, R, U, kGate>;                               \
+    if (tq_status st = allow_dynamic_lds((const void *)k, (int)lds))       \
+      return st;                                                           \
+    return launch(k, grid, block, lds, s, a);                              \
+  }
+  TQ_GEMV_CASE(64, 2, 4)
+  TQ_GEMV_CASE(32, 2, 4)
+  TQ_GEMV_CASE(16, 2, 4)
+  TQ_GEMV_CASE(64, 1, 4)
+  TQ_GEMV_CASE(32, 1, 4)
+  TQ_GEMV_CASE(16, 1, 4)
+#undef TQ_GEMV_CASE
+  return TQ_ERR_LAUNCH;
+}
+
+}  // namespace
+
+// Shared by tq_gemv and the M = 1 branch of tq_gate_up_relu2.
+tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
+                  const int8_t *xq, const float *x_scale, int64_t N, int64_t K,
+                  float *y, int32_t *acc0, int32_t *acc1, hipStream_t stream) {
+  DeviceInfo dev;
+  if (tq_status s = current_device(&dev)) return s;
+  const bool gate = p1 != nullptr;
+  GemvArgs a;
+  a.p0 = p0;
+  a.p1 = p1;
+  a.s0 = s0;
+  a.s1 = s1;
+  a.xq = xq;
+  a.x_scale = x_scale;
+  a.n4 = (int)(N / 4);
+  a.kp = (int)(K / 16);
+  a.y = y;
+  a.acc0 = acc0;
+  a.acc1 = acc1;
+  const GemvPlan pl = plan_gemv(a.n4, a.kp, dev.num_cus, gate ? 2 : 1);
+  const size_t lds = (size_t)K;
+  return gate ? launch_gemv<true>(pl, a, lds, stream)
+              : launch_gemv<false>(pl, a, lds, stream);
+}
+
+}  // namespace tq
+
+extern "C" tq_status tq_gemv(const uint8_t *packed, float w_scale,
+                             const int8_t *xq, const float *x_scale, int64_t N,
+                             int64_t K, float *y, int32_t *acc,
+                             hipStream_t stream) {
+  using namespace tq;
+  if (tq_status s = check_nk(N, K)) return s;
+  if (N == 0) return TQ_OK;
+  if (!y || !x_scale || (K > 0 && (!packed || !xq))) return TQ_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(y, 4) ||
+      !aligned(acc, 4) || !aligned(x_scale, 4))
+    return TQ_ERR_ALIGN;
+  return gemv_m1(packed, w_scale, nullptr, 0.0f, xq, x_scale, N, K, y, acc,
+                 nullptr, stream);
+}

@@ -1,0 +1,159 @@
+/*
+ * tq.h -- C ABI of the ternary GEMV library (libtq.so) for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The library computes the BitNet b1.58 ternary matrix-vector product at
+ * decode and its small-batch and gated-MLP variants.  Pages cited by title:
+ *   [ISSUE]  "Feature request: BitNet 1.58-bit ternary inference on ROCm
+ *            (gfx1151)" -- section "Architecture" (ternary weights stored
+ *            as uint8, four values per byte; squared-ReLU MLP) and section
+ *            "Weight mapping (bitnet-b1.58-2B-4T)" (a projection [N,K] is
+ *            held as a [N/4,K] uint8 array; per-tensor .weight_scale keys
+ *            are named in "What We Need").
+ *   [ARC]    "the full arc: how the 1bit.systems ternary stack got from
+ *            broken to 76.7 tok/s" -- TL;DR (a hand-tuned ternary GEMV
+ *            near the memory-bandwidth peak is the decode hot loop).
+ *   [DIGEST] "BitNet" news-digest tag page, first item: weights in {-1,0,1}
+ *            replace multiplies with adds and subtracts.
+ *
+ * Data conventions (shared by every call):
+ *   - W is an [N,K] matrix of ternary weights w in {-1,0,+1}.  Packed form:
+ *     uint8 [N/4,K], row-major (K contiguous).  Byte [i,k] holds, in bits
+ *     2j..2j+1 (j = 0..3, least significant pair first), the code w+1 of
+ *     row n = j*(N/4) + i, column k.  Code 3 is reserved.  (The page fixes
+ *     the [N/4,K] uint8 shape; the code and the row-to-bit assignment are
+ *     this library's reading.)
+ *   - s_w: one fp32 weight scale per tensor, passed by value; the real
+ *     weight is s_w * w.
+ *   - Activations x: [M,K] row-major, bf16 or fp32.  Each row m is quantized
+ *     to int8 by its absmax: a = max_k |x[m,k]|, a' = max(a, 1e-5),
+ *     inv = 127/a' (fp32, correctly rounded), q = clamp(rne(x*inv), +-127)
+ *     with rne = round half to even, and s_x[m] = a'/127 (fp32).
+ *   - Products are exact: acc[m,n] = sum_k w[n,k]*q[m,k] in int32.
+ *   - Rescale: y[m,n] = (float)acc[m,n] * (s_w * s_x[m]), each product
+ *     rounded once to fp32, in that order.  Results are bit-reproducible.
+ *
+ * Memory and streams:
+ *   - Every array argument is caller-owned DEVICE memory on the current HIP
+ *     device.  The library allocates and frees nothing and keeps no state
+ *     beyond a per-device cache of the compute-unit count.
+ *   - Every call enqueues its work on `stream` (NULL = the default stream)
+ *     and returns without synchronizing.  Calls are thread-safe.
+ *
+ * Errors: a call returns a tq_status synchronously.  Host-detectable
+ * problems (null pointer, bad shape, misalignment, bad dtype, no device) are
+ * reported before anything is enqueued; nothing is launched then.
+ * TQ_ERR_LAUNCH reports a failed kernel launch.  Faults during execution
+ * surface at the caller's next synchronization, as in HIP.
+ *
+ * Shape rules: N % 4 == 0; K % 16 == 0; 0 <= K <= TQ_MAX_K;
+ * 1 <= M <= TQ_MAX_M where M is an argument.  N == 0 or M == 0 is a no-op
+ * returning TQ_OK.  K == 0 is allowed (empty sums: acc = 0).
+ * Alignment: packed, xq and x 16-byte aligned; y, acc, h, x_scale 4-byte.
+ * Inputs must be finite; NaN/Inf activations are outside the contract.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported entry points (the library is built with hidden visibility). */
+#define TQ_API __attribute__((visibility("default")))
+
+/* HIP's stream handle (identical to the typedef in hip_runtime_api.h). */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum tq_status {
+    TQ_OK = 0,
+    TQ_ERR_NULL = 1,    /* a required pointer is NULL */
+    TQ_ERR_SHAPE = 2,   /* size out of range or not a required multiple */
+    TQ_ERR_ALIGN = 3,   /* pointer not aligned as required */
+    TQ_ERR_DTYPE = 4,   /* unknown tq_dtype */
+    TQ_ERR_DEVICE = 5,  /* no usable HIP device */
+    TQ_ERR_LAUNCH = 6   /* the kernel launch failed */
+} tq_status;
+
+typedef enum tq_dtype {
+    TQ_BF16 = 0,
+    TQ_F32 = 1
+} tq_dtype;
+
+/* Largest K: 127*K stays below 2^24, so (float)acc is exact, and the int8
+   activation row fits the kernels' LDS staging. */
+#define TQ_MAX_K 131072
+/* Largest activation batch of tq_gemm_small / tq_gate_up_relu2. */
+#define TQ_MAX_M 64
+
+/*
+ * tq_pack -- pack ternary weights ([ISSUE] "Architecture": uint8, four
+ * values per byte; "Weight mapping": [N,K] -> [N/4,K]).
+ *   w       int8 [N,K], values in {-1,0,1}; any other value is written as
+ *           the reserved code 3 (outside the contract of every other call).
+ *   packed  uint8 [N/4,K], output, 16-byte aligned.
+ */
+TQ_API tq_status tq_pack(const int8_t *w, int64_t N, int64_t K, uint8_t *packed,
+                  hipStream_t stream);
+
+/*
+ * tq_act_quant -- per-token absmax int8 quantization of activations
+ * (the conventions above).
+ *   x        [M,K] bf16 (xt = TQ_BF16) or fp32 (xt = TQ_F32), 16-B aligned.
+ *   xq       int8 [M,K], output, 16-B aligned.
+ *   x_scale  fp32 [M], output: s_x[m] = a'/127.
+ *   M        1..TQ_MAX_M.
+ */
+TQ_API tq_status tq_act_quant(const void *x, tq_dtype xt, int64_t M, int64_t K,
+                       int8_t *xq, float *x_scale, hipStream_t stream);
+
+/*
+ * tq_gemv -- the ternary matrix-vector product at M = 1 ([ARC] TL;DR:
+ * the decode hot loop; [DIGEST]: add/subtract/skip per weight).
+ *   packed   uint8 [N/4,K] (16-B aligned), w_scale = s_w.
+ *   xq       int8 [K] (16-B aligned), x_scale fp32 [1] (device).
+ *   y        fp32 [N], output: y[n] = (float)acc[n] * (s_w * x_scale[0]).
+ *   acc      int32 [N], optional output of the exact sums (NULL = skip).
+ */
+TQ_API tq_status tq_gemv(const uint8_t *packed, float w_scale, const int8_t *xq,
+                  const float *x_scale, int64_t N, int64_t K, float *y,
+                  int32_t *acc, hipStream_t stream);
+
+/*
+ * tq_gemm_small -- the same product for a small batch of activation rows
+ * (batched decode / short prefill), on the int8 matrix cores.
+ *   xq       int8 [M,K] (16-B aligned), x_scale fp32 [M].
+ *   y        fp32 [M,N], output: y[m,n] = (float)acc[m,n]*(s_w*x_scale[m]).
+ *   acc      int32 [M,N], optional (NULL = skip).
+ *   M        1..TQ_MAX_M.
+ */
+TQ_API tq_status tq_gemm_small(const uint8_t *packed, float w_scale, const int8_t *xq,
+                        const float *x_scale, int64_t M, int64_t N, int64_t K,
+                        float *y, int32_t *acc, hipStream_t stream);
+
+/*
+ * tq_gate_up_relu2 -- fused gate and up projections with the squared-ReLU
+ * gate ([ISSUE] "Architecture": relu_squared in place of SiLU):
+ *   g = gemm(packed_gate, s_gate), u = gemm(packed_up, s_up) on the same xq,
+ *   h[m,n] = (r*r) * u[m,n] with r = g[m,n] > 0 ? g[m,n] : 0 (fp32).
+ *   packed_gate, packed_up  uint8 [N/4,K] each (16-B aligned).
+ *   xq int8 [M,K], x_scale fp32 [M]; h fp32 [M,N] output.
+ *   acc_gate, acc_up  int32 [M,N], optional exact sums (NULL = skip).
+ *   M  1..TQ_MAX_M (M = 1 uses the GEMV kernels, M > 1 the matrix cores).
+ */
+TQ_API tq_status tq_gate_up_relu2(const uint8_t *packed_gate, float s_gate,
+                           const uint8_t *packed_up, float s_up,
+                           const int8_t *xq, const float *x_scale, int64_t M,
+                           int64_t N, int64_t K, float *h, int32_t *acc_gate,
+                           int32_t *acc_up, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+TQ_API const char *tq_status_string(tq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: libtq.so loads, exports every entry point
+include/tq.h declares, and rejects every host-detectable bad argument before
+any HIP call (so nothing is launched).  Pointers below are fake addresses;
+every call here fails validation (or is a documented no-op) before any
+pointer could be dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, DEVICE, LAUNCH = range(7)
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import bit_gemv_tq_amd
+    return bit_gemv_tq_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"TQ_API\s+[\w\s\*]+?\b(tq_\w+)\s*\(", text)
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    assert set(names) == {"tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
+                          "tq_gate_up_relu2", "tq_status_string"}
+
+
+def test_library_exports_every_declared_symbol(tq):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", tq.LIB_PATH],
+                                  text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(tq.lib, name) is not None
+    assert exported == set(declared_functions())   # nothing else leaks
+    assert set(tq.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(tq):
+    for s in range(7):
+        assert tq.lib.tq_status_string(s)
+    assert b"unknown" in tq.lib.tq_status_string(99)
+
+
+P = ctypes.c_void_p
+A = P(0x10000)          # 64 KiB-aligned fake device address
+MIS = P(0x10004)        # 4-aligned, not 16-aligned
+ODD = P(0x10001)
+
+
+def gemv(tq, packed=A, xq=A, xs=A, N=64, K=64, y=A, acc=None):
+    return tq.lib.tq_gemv(packed, 0.02, xq, xs, N, K, y, acc, None)
+
+
+def test_gemv_validation(tq):
+    assert gemv(tq, N=6) == SHAPE
+    assert gemv(tq, N=-4) == SHAPE
+    assert gemv(tq, K=24) == SHAPE
+    assert gemv(tq, K=131072 + 16) == SHAPE
+    assert gemv(tq, K=-16) == SHAPE
+    assert gemv(tq, y=None) == NULL
+    assert gemv(tq, xs=None) == NULL
+    assert gemv(tq, packed=None) == NULL
+    assert gemv(tq, xq=None) == NULL
+    assert gemv(tq, packed=MIS) == ALIGN
+    assert gemv(tq, xq=MIS) == ALIGN
+    assert gemv(tq, y=ODD) == ALIGN
+    assert gemv(tq, acc=ODD) == ALIGN
+    assert gemv(tq, N=0) == OK                    # empty: no-op
+
+
+def test_act_quant_validation(tq):
+    f = tq.lib.tq_act_quant
+    assert f(A, 2, 1, 64, A, A, None) == DTYPE
+    assert f(A, 0, 65, 64, A, A, None) == SHAPE
+    assert f(A, 0, -1, 64, A, A, None) == SHAPE
+    assert f(A, 0, 1, 40, A, A, None) == SHAPE
+    assert f(A, 1, 1, 131072 + 16, A, A, None) == SHAPE
+    assert f(A, 0, 1, 64, None, A, None) == NULL
+    assert f(A, 0, 1, 64, A, None, None) == NULL
+    assert f(MIS, 0, 1, 64, A, A, None) == ALIGN
+    assert f(A, 0, 1, 64, MIS, A, None) == ALIGN
+    assert f(A, 0, 0, 64, A, A, None) == OK
+
+
+def test_gemm_small_and_gate_validation(tq):
+    g = tq.lib.tq_gemm_small
+    assert g(A, 0.02, A, A, 65, 64, 64, A, None, None) == SHAPE
+    assert g(A, 0.02, A, A, 4, 62, 64, A, None, None) == SHAPE
+    assert g(A, 0.02, A, A, 4, 64, 72, A, None, None) == SHAPE
+    assert g(A, 0.02, MIS, A, 4, 64, 64, A, None, None) == ALIGN
+    assert g(A, 0.02, A, A, 4, 64, 64, None, None, None) == NULL
+    assert g(A, 0.02, A, A, 0, 64, 64, A, None, None) == OK
+    h = tq.lib.tq_gate_up_relu2
+    assert h(A, 0.02, None, 0.02, A, A, 4, 64, 64, A, None, None, None) == NULL
+    assert h(A, 0.02, MIS, 0.02, A, A, 4, 64, 64, A, None, None, None) == ALIGN
+    assert h(A, 0.02, A, 0.02, A, A, 4, 64, 64, A, ODD, None, None) == ALIGN
+    assert h(A, 0.02, A, 0.02, A, A, 4, 64, 64, A, None, ODD, None) == ALIGN
+    assert h(A, 0.02, A, 0.02, A, A, 99, 64, 64, A, None, None, None) == SHAPE
+
+
+def test_pack_validation(tq):
+    f = tq.lib.tq_pack
+    assert f(A, 5, 16, A, None) == SHAPE
+    assert f(A, 8, 8, A, None) == SHAPE
+    assert f(None, 8, 16, A, None) == NULL
+    assert f(A, 8, 16, MIS, None) == ALIGN
+    assert f(A, 0, 16, A, None) == OK
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device path")
+def test_no_device_is_reported(tq):
+    # Valid arguments on a machine with no GPU: TQ_ERR_DEVICE, nothing runs.
+    assert gemv(tq) == DEVICE
+    assert tq.lib.tq_act_quant(A, 0, 1, 64, A, A, None) == DEVICE
+    assert tq.lib.tq_pack(A, 8, 16, A, None) == DEVICE
+    assert tq.lib.tq_gemm_small(A, 0.02, A, A, 4, 64, 64, A, None, None) == DEVICE
+
+
+def test_binding_rejects_host_tensors(tq):
+    import torch
+    w = torch.zeros(8, 16, dtype=torch.int8)
+    with pytest.raises(ValueError):
+        tq.tq_pack(w)
+    with pytest.raises(TypeError):
+        tq.tq_pack(w.to(torch.int32))
+    with pytest.raises(TypeError):
+        tq.tq_act_quant(torch.zeros(16, dtype=torch.float16))

@@ -1,0 +1,266 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded
+inputs.  Integer results (packed bytes, int8 activations, int32 sums) must be
+bit-exact; fp32 results must be within 1e-6 relative of the oracle's exact
+(fp64) value and, with the fixed operation order of the rescale, are also
+expected bit-exact against the oracle's fp32 path.
+
+Sizes span several tiles with ragged tails (N/4 not a multiple of a block's
+rows, K/16 not a multiple of a lane group), the maximum K, empty shapes, and
+the full 2B-4T and 70B-class layer shapes in the launch configuration the
+benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-6
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import bit_gemv_tq_amd as tq
+    import oracle
+    return torch, tq, oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_packed(env, codes):
+    """Pack on the GPU and check the bytes against the oracle's packing."""
+    torch, tq, oracle = env
+    w = torch.from_numpy(codes).cuda()
+    packed = tq.tq_pack(w)
+    ref = oracle.pack(codes)
+    got = packed.cpu().numpy()
+    np.testing.assert_array_equal(got, ref)
+    return packed, ref
+
+
+def quantized(env, xbits, M, K):
+    """bf16 activations -> (GPU xq, GPU s_x), checked bit-exact vs oracle."""
+    torch, tq, oracle = env
+    x = torch.from_numpy(xbits.view(np.int16)).view(torch.bfloat16).cuda().reshape(M, K)
+    xq, xs = tq.tq_act_quant(x)
+    q_ref, s_ref = oracle.act_quant(xbits.reshape(M, K), "bf16")
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32),
+                                  s_ref.view(np.uint32))
+    return xq, xs, q_ref, s_ref
+
+
+def check_y(y_gpu, y32_ref, y64_ref):
+    y = y_gpu.reshape(y32_ref.shape).astype(np.float64)
+    err = np.abs(y - y64_ref)
+    assert np.all(err <= REL_TOL * np.abs(y64_ref)), float(
+        np.max(err / np.maximum(np.abs(y64_ref), 1e-300)))
+    np.testing.assert_array_equal(y_gpu.reshape(y32_ref.shape).view(np.uint32),
+                                  y32_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ pack
+@pytest.mark.parametrize("N,K", [(4, 16), (8, 32), (20, 48), (100, 1008),
+                                 (640, 2560), (6912, 2560), (2560, 6912)])
+def test_pack(env, N, K):
+    say(f"pack N={N} K={K}")
+    dev_packed(env, workloads.ternary_codes(N, K, seed=N + K))
+
+
+def test_pack_reserved_code(env):
+    torch, tq, _ = env
+    w = torch.zeros(4, 16, dtype=torch.int8)
+    w[2, 5] = 7
+    w[0, 0] = -1
+    p = tq.tq_pack(w.cuda()).cpu().numpy()
+    assert (p[0, 5] >> 4) & 3 == 3           # row 2 = plane 2 of packed row 0
+    assert p[0, 0] & 3 == 0 and (p[0, 0] >> 2) & 3 == 1
+
+
+# ------------------------------------------------------------------ act quant
+@pytest.mark.parametrize("M,K", [(1, 16), (1, 2560), (4, 2560), (16, 6912),
+                                 (64, 2560), (3, 28672), (1, 131072)])
+def test_act_quant_bf16(env, M, K):
+    say(f"act_quant bf16 M={M} K={K}")
+    xb = workloads.activations_bf16(M, K, seed=M * 7 + K, outliers=True)
+    quantized(env, xb, M, K)
+
+
+@pytest.mark.parametrize("M,K", [(1, 2560), (5, 6912), (64, 160)])
+def test_act_quant_f32(env, M, K):
+    torch, tq, oracle = env
+    say(f"act_quant f32 M={M} K={K}")
+    x = workloads.normal_f32(M, K, seed=K + M, outliers=True) * np.float32(0.37)
+    xq, xs = tq.tq_act_quant(torch.from_numpy(x).cuda())
+    q_ref, s_ref = oracle.act_quant(x, "f32")
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(xs.cpu().numpy(), s_ref)
+
+
+def test_act_quant_exhaustive_bf16(env):
+    # Every finite bf16 value, quantized against 64 different absmax values
+    # (tiny to huge, including below the 1e-5 floor).
+    torch, tq, oracle = env
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    xs = (bits << 16).view(np.float32)
+    xs = xs[np.isfinite(xs)]
+    K = (xs.size + 16) // 16 * 16
+    amax = np.float32(2.0) ** np.linspace(-30, 60, 64).astype(np.float32)
+    amax[0] = np.float32(3e-6)
+    rows = np.zeros((64, K), np.float32)
+    for m in range(64):
+        a = np.float32(amax[m])
+        rows[m, 0] = a
+        rows[m, 1:1 + xs.size] = np.clip(xs, -a, a)
+    rb = workloads.to_bf16_bits(rows)
+    say(f"act_quant exhaustive bf16 M=64 K={K}")
+    quantized(env, rb, 64, K)
+
+
+def test_act_quant_scale_sweep(env):
+    # s_x = a'/127 and the quantization at inexact 127/a' for every positive
+    # finite bf16 absmax: 16 values per row near rounding ties.
+    torch, tq, oracle = env
+    bits = np.arange(1 << 15, dtype=np.uint32)
+    a_all = (bits << 16).view(np.float32)
+    a_all = a_all[np.isfinite(a_all) & (a_all > 0)]
+    frac = (np.arange(15, dtype=np.float32) + np.float32(0.5)) / np.float32(15.3)
+    for c0 in range(0, a_all.size, 64):
+        a = a_all[c0:c0 + 64]
+        rows = np.zeros((a.size, 16), np.float32)
+        rows[:, 0] = a
+        rows[:, 1:] = a[:, None] * frac[None, :]
+        rb = workloads.to_bf16_bits(rows)
+        quantized(env, rb, a.size, 16)
+
+
+# ------------------------------------------------------------------ gemv
+GEMV_SHAPES = [(4, 16), (8, 32), (12, 48), (100, 1008), (36, 2064), (260, 400),
+               (2560, 2560), (640, 2560), (6912, 2560), (2560, 6912),
+               (4, 131072), (2052, 16)]
+
+
+def run_gemv(env, N, K, seed, s_w=np.float32(0.02)):
+    torch, tq, oracle = env
+    codes = workloads.ternary_codes(N, K, seed=seed)
+    packed, ref_packed = dev_packed(env, codes)
+    xb = workloads.activations_bf16(1, K, seed=seed + 1, outliers=True)
+    xq, xs, q_ref, s_ref = quantized(env, xb, 1, K)
+    acc = torch.empty(N, dtype=torch.int32, device="cuda")
+    y = tq.tq_gemv(packed, s_w, xq, xs, acc=acc)
+    torch.cuda.synchronize()
+    acc_ref, y32 = oracle.gemv(ref_packed, s_w, q_ref, s_ref, N)
+    y64 = oracle.rescale(acc_ref, s_w, s_ref, exact=True)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref[0])
+    check_y(y.cpu().numpy(), y32[0], y64[0])
+    return packed, xq, xs, y
+
+
+@pytest.mark.parametrize("N,K", GEMV_SHAPES)
+def test_gemv(env, N, K):
+    say(f"gemv N={N} K={K}")
+    run_gemv(env, N, K, seed=N * 3 + K)
+
+
+@pytest.mark.parametrize("name", ["70b_up", "70b_down", "8b_up", "8b_down"])
+def test_gemv_large(env, name):
+    N, K = workloads.LARGE_SHAPES[name]
+    say(f"gemv {name} N={N} K={K}")
+    run_gemv(env, N, K, seed=workloads.seed_for(4, list(workloads.LARGE_SHAPES).index(name)))
+
+
+def test_gemv_deterministic_and_scales(env):
+    torch, tq, oracle = env
+    packed, xq, xs, y = run_gemv(env, 2560, 2560, seed=5, s_w=np.float32(-0.75))
+    y2 = tq.tq_gemv(packed, np.float32(-0.75), xq, xs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32),
+                                  y2.cpu().numpy().view(np.uint32))
+
+
+def test_gemv_zero_k_and_empty(env):
+    torch, tq, _ = env
+    packed = torch.empty(4, 0, dtype=torch.uint8, device="cuda")
+    xq = torch.empty(0, dtype=torch.int8, device="cuda")
+    xs = torch.ones(1, dtype=torch.float32, device="cuda")
+    y = torch.full((16,), 7.0, device="cuda")
+    acc = torch.full((16,), 7, dtype=torch.int32, device="cuda")
+    tq.tq_gemv(packed, 0.5, xq, xs, y, acc)
+    torch.cuda.synchronize()
+    assert not y.any() and not acc.any()
+    packed = torch.empty(0, 64, dtype=torch.uint8, device="cuda")
+    tq.tq_gemv(packed, 0.5, torch.zeros(64, dtype=torch.int8, device="cuda"), xs)
+
+
+# ------------------------------------------------------------------ gate/up
+@pytest.mark.parametrize("M,N,K", [(1, 6912, 2560), (1, 20, 48), (1, 100, 1008),
+                                   (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560)])
+def test_gate_up_relu2(env, M, N, K):
+    torch, tq, oracle = env
+    say(f"gate_up M={M} N={N} K={K}")
+    cg = workloads.ternary_codes(N, K, seed=4 + N)
+    cu = workloads.ternary_codes(N, K, seed=5 + N)
+    pg, rg = dev_packed(env, cg)
+    pu, ru = dev_packed(env, cu)
+    xb = workloads.activations_bf16(M, K, seed=K + M, outliers=True)
+    xq, xs, q_ref, s_ref = quantized(env, xb, M, K)
+    s_g, s_u = workloads.tensor_scale(4), workloads.tensor_scale(5)
+    acc_g = torch.empty(M, N, dtype=torch.int32, device="cuda")
+    acc_u = torch.empty(M, N, dtype=torch.int32, device="cuda")
+    h = tq.tq_gate_up_relu2(pg, s_g, pu, s_u, xq, xs, acc_gate=acc_g, acc_up=acc_u)
+    torch.cuda.synchronize()
+    ag, au, h32 = oracle.gate_up_relu2(rg, s_g, ru, s_u, q_ref, s_ref, N)
+    _, _, h64 = oracle.gate_up_relu2(rg, s_g, ru, s_u, q_ref, s_ref, N, exact=True)
+    np.testing.assert_array_equal(acc_g.cpu().numpy(), ag)
+    np.testing.assert_array_equal(acc_u.cpu().numpy(), au)
+    hg = h.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(h.cpu().numpy().view(np.uint32), h32.view(np.uint32))
+    assert np.all(np.abs(hg - h64) <= REL_TOL * np.abs(h64))
+
+
+# ------------------------------------------------------------------ gemm small
+GEMM_CASES = [(m, 6912, 2560) for m in (2, 4, 16, 64)] + \
+             [(m, 2560, 6912) for m in (4, 16, 64)] + \
+             [(3, 20, 48), (5, 68, 80), (17, 260, 400), (33, 100, 1008),
+              (63, 64, 16), (48, 2052, 112)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+def test_gemm_small(env, M, N, K):
+    torch, tq, oracle = env
+    say(f"gemm_small M={M} N={N} K={K}")
+    codes = workloads.ternary_codes(N, K, seed=M + N + K)
+    packed, ref = dev_packed(env, codes)
+    xb = workloads.activations_bf16(M, K, seed=M * 11 + K, outliers=True)
+    xq, xs, q_ref, s_ref = quantized(env, xb, M, K)
+    acc = torch.empty(M, N, dtype=torch.int32, device="cuda")
+    s_w = workloads.tensor_scale(6)
+    y = tq.tq_gemm_small(packed, s_w, xq, xs, acc=acc)
+    torch.cuda.synchronize()
+    acc_ref, y32 = oracle.gemv(ref, s_w, q_ref, s_ref, N)
+    y64 = oracle.rescale(acc_ref, s_w, s_ref, exact=True)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    check_y(y.cpu().numpy(), y32, y64)
+    # Row m of the batch equals the M = 1 GEMV of row m, bit for bit.
+    for m in (0, M - 1):
+        ym = tq.tq_gemv(packed, s_w, xq[m].contiguous(), xs[m:m + 1].contiguous())
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ym.cpu().numpy().view(np.uint32),
+                                      y[m].cpu().numpy().view(np.uint32))
+
+
+def test_gemm_small_zero_k(env):
+    torch, tq, _ = env
+    packed = torch.empty(8, 0, dtype=torch.uint8, device="cuda")
+    xq = torch.empty(5, 0, dtype=torch.int8, device="cuda")
+    xs = torch.ones(5, dtype=torch.float32, device="cuda")
+    y = tq.tq_gemm_small(packed, 0.5, xq, xs)
+    torch.cuda.synchronize()
+    assert y.shape == (5, 32) and not y.any()
