@@ -1,26 +1,34 @@
 """Benchmark of the ternary GEMV hot path at M = 1 on one MI355X.
 
-A step is one pass of the hot path over the workload the metric names:
-for each of the shapes [N, K] = [2560, 6912] (2B-4T down projection),
-[28672, 8192] and [8192, 28672] (70B-class layer, both orientations):
-per-token int8 quantization of a bf16 activation (tq_act_quant), then the
-ternary GEMV with its fp32 rescale (tq_gemv).  Weights are seeded synthetic
-ternary codes (P(0) = 0.35), packed on the GPU; activations are bf16 N(0,1).
+Step (the `value` line): one pass of the hot path over the shapes the metric
+names, [N, K] = [2560, 6912] (2B-4T down projection) and [8192, 28672]
+(70B-class down projection), plus the transposed 70B-class shape
+[28672, 8192]: for each, per-token int8 quantization of a bf16 activation
+(tq_act_quant) then the ternary GEMV with its fp32 rescale (tq_gemv).
+`value` = packed weight bytes per step / step time (GB/s).
 
-Measurement:
-  * Weights come from a pool of distinct buffers (>= 1 GiB) cycled step by
-    step, so the 256 MB Infinity Cache cannot serve repeats.
-  * Each pool set's step is captured in a HIP graph; the timed region replays
-    K graphs.  A spin kernel queued just before the start event keeps the host
-    ahead of the GPU, so HIP events measure GPU execution only.
-  * The dominant kernel (the GEMV instantiation that runs both 70B-class
-    shapes) is timed per launch with event pairs on its stream; its
-    algorithmic bytes (packed weights + int8 activations + scale + fp32
-    outputs) over that time give roofline.achieved against 8 TB/s.
-  * cpu_baseline: the CPU oracle (plain C, one thread) on the same step for
-    one pool set, repeated for about 10 s.
+Inputs: seeded synthetic ternary weights (P(0) = 0.35), packed on the GPU
+by tq_pack; bf16 N(0,1) activations.  Everything is resident in HBM before
+timing starts.
 
-Prints one JSON line.
+Timing:
+  * Each shape has a pool of distinct packed copies of at least 640 MB, so
+    the 256 MB Infinity Cache cannot serve repeats; step i uses copy i mod C.
+  * Steps and kernel loops are captured in HIP graphs; a spin kernel queued
+    before the start event keeps the host ahead, so HIP events on the
+    launch stream measure GPU execution only.
+  * roofline: the dominant kernel (the [8192, 28672] GEMV) is timed as a
+    graph of back-to-back launches over its pool; algorithmic bytes per
+    launch (packed weights + int8 x + fp32 scale + fp32 y) / time per
+    launch, against 8 TB/s.  Back-to-back time includes the short gap
+    between graph nodes, so it is an upper bound on the kernel duration
+    that rocprofv3's kernel trace reports.
+  * rows: every hot-path row timed the same way -- act_quant, gemv, fused
+    gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64) and the
+    30-layer decode-step chain (graph-captured).
+  * cpu_baseline: the CPU oracle (plain C, one thread) on one step, repeated
+    for about 10 s.
+Prints one JSON line on stdout; progress on stderr.
 """
 from __future__ import annotations
 
@@ -38,13 +46,17 @@ if ROOT not in sys.path:
 
 METRIC = ("ternary GEMV weight GB/s + % of MI355X HBM peak at M=1 "
           "(2560x6912, 8192x28672)")
-SHAPES = {"down_2b4t": (2560, 6912), "70b_up": (28672, 8192),
-          "70b_down": (8192, 28672)}
-DOMINANT = ("70b_up", "70b_down")
+SHAPES = {"down_2b4t": (2560, 6912), "70b_down": (8192, 28672),
+          "70b_up": (28672, 8192)}
+DOMINANT = "70b_down"
 HBM_PEAK_GBS = 8000.0
-POOL_BYTES_MIN = 1 << 30
-COUNTER_FILE = os.path.join(ROOT, "profiles", "tq_gemv_70b_counters.txt")
-KERNEL_SOURCES = ("bit_gemv_tq_amd/csrc/tq_gemv.hip",
+INT8_MFMA_PEAK_TOPS = 5000.0
+POOL_BYTES_MIN = 640 << 20
+STEP_COPIES = 12
+SPIN = 20_000_000
+COUNTER_FILE = os.path.join(ROOT, "profiles", "tq_gemv_8192x28672_counters.txt")
+KERNEL_SOURCES = ("bit_gemv_tq_amd/csrc/tq_gemv_reg.h",
+                  "bit_gemv_tq_amd/csrc/tq_gemv.hip",
                   "bit_gemv_tq_amd/csrc/tq_device.h")
 
 
@@ -56,9 +68,9 @@ def weight_bytes(N, K):
     return N * K // 4
 
 
-def algo_bytes(N, K):
+def algo_bytes(N, K, M=1):
     # packed weights + int8 activations + fp32 x_scale + fp32 outputs
-    return N * K // 4 + K + 4 + 4 * N
+    return N * K // 4 + M * K + 4 * M + 4 * M * N
 
 
 def kernel_source_hash():
@@ -88,7 +100,7 @@ def read_traffic():
 
 
 def cpu_baseline(budget_s=10.0):
-    """The CPU oracle on one step of the same workload (one pool set)."""
+    """The CPU oracle on one step of the same workload."""
     import numpy as np
 
     import oracle
@@ -113,8 +125,45 @@ def cpu_baseline(budget_s=10.0):
     return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s",
             "cores": 1, "kind": "oracle",
             "sample": (f"{reps} full steps (all three shapes, act_quant + GEMV) "
-                       f"in {el:.1f} s, one thread, {platform.processor() or platform.machine()}, "
-                       f"{os.cpu_count()} host cores visible")}
+                       f"in {el:.1f} s on one thread ({platform.machine()}, "
+                       f"{os.cpu_count()} host cores visible)")}
+
+
+class Timer:
+    """Graph-captured launch sequences timed with HIP events."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def graph(self, fn):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graphs(self, graphs, reps):
+        """ms per replay, cycling through `graphs` for `reps` replays."""
+        torch = self.torch
+        for g in graphs[:2]:
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN)
+        e0.record()
+        for i in range(reps):
+            graphs[i % len(graphs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
 
 
 def main():
@@ -124,8 +173,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--kernel-reps", type=int, default=100,
-                    help="per-shape event-timed launches for the kernel table")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-row table (gate/up, GEMM, chain)")
+    ap.add_argument("--kernel-reps", type=int, default=96,
+                    help="launches per graph in the per-kernel loops")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run a 256 MiB calibration copy and the dominant "
+                         "kernel (for rocprofv3 --pmc runs), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -140,21 +194,27 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    timer = Timer(torch)
     s_w = np.float32(0.02)
 
-    # ---------------------------------------------------------------- pool
-    set_bytes = sum(weight_bytes(*s) for s in SHAPES.values())
-    n_sets = max(2, -(-POOL_BYTES_MIN // set_bytes))
-    log(f"building weight pool: {n_sets} sets x {set_bytes / 1e6:.1f} MB")
-    pool = []
-    for i in range(n_sets):
-        d = {}
-        for t, (name, (N, K)) in enumerate(SHAPES.items()):
-            w = workloads.ternary_codes_torch(N, K, seed=workloads.seed_for(4, t, i) + 7919,
-                                              device=dev)
-            d[name] = tq.tq_pack(w)
+    if args.counters:
+        counters_run(torch, tq, workloads, dev)
+        return
+
+    # ---------------------------------------------------------------- pools
+    def make_pool(N, K, copies, seed0):
+        out = []
+        for c in range(copies):
+            w = workloads.ternary_codes_torch(N, K, seed=seed0 + c, device=dev)
+            out.append(tq.tq_pack(w))
             del w
-        pool.append(d)
+        return out
+
+    pools = {}
+    for t, (name, (N, K)) in enumerate(SHAPES.items()):
+        copies = max(STEP_COPIES, -(-POOL_BYTES_MIN // weight_bytes(N, K)))
+        log(f"pool {name}: {copies} copies x {weight_bytes(N, K) / 1e6:.1f} MB")
+        pools[name] = make_pool(N, K, copies, workloads.seed_for(4, t) * 1000 + 7)
     torch.cuda.synchronize()
     x, xq, xs, y = {}, {}, {}, {}
     for t, (name, (N, K)) in enumerate(SHAPES.items()):
@@ -164,83 +224,54 @@ def main():
         xs[name] = torch.empty(1, dtype=torch.float32, device=dev)
         y[name] = torch.empty(N, dtype=torch.float32, device=dev)
 
-    def step(i, stream=None):
-        P = pool[i % n_sets]
+    def step(i):
         for name in SHAPES:
-            tq.tq_act_quant(x[name], xq[name], xs[name], stream=stream)
-            tq.tq_gemv(P[name], s_w, xq[name], xs[name], y[name], stream=stream)
+            tq.tq_act_quant(x[name], xq[name], xs[name])
+            tq.tq_gemv(pools[name][i % STEP_COPIES], s_w, xq[name], xs[name], y[name])
 
-    # ---------------------------------------------------------------- graphs
+    # ---------------------------------------------------------------- step
     log("capturing step graphs")
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(0)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graphs = []
-    for i in range(n_sets):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(i)
-        graphs.append(g)
-    torch.cuda.synchronize()
-
+    graphs = [timer.graph(lambda i=i: step(i)) for i in range(STEP_COPIES)]
     for i in range(args.warmup):
-        graphs[i % n_sets].replay()
-    torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- timed
-    spin = 50_000_000  # ~20 ms of spinning: the host queues ahead meanwhile
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+        graphs[i % STEP_COPIES].replay()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    torch.cuda._sleep(spin)
-    ev0.record()
-    for i in range(args.steps):
-        graphs[i % n_sets].replay()
-    ev1.record()
-    torch.cuda.synchronize()
+    ms_step = timer.time_graphs(graphs, args.steps)
     wall = time.perf_counter() - wall0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    step_wbytes = set_bytes
+    step_wbytes = sum(weight_bytes(*s) for s in SHAPES.values())
     value = step_wbytes / (ms_step * 1e-3) / 1e9
+    log(f"step: {ms_step * 1e3:.2f} us -> {value:.0f} GB/s")
 
-    # ------------------------------------------------- per-kernel timing
-    # Event pairs around single launches on the current stream, queued
-    # behind a spin so that the host is ahead of the GPU.
+    # ------------------------------------------------- per-kernel loops
+    R = args.kernel_reps
+
+    def gemv_loop(name, start):
+        P = pools[name]
+        for r in range(R):
+            tq.tq_gemv(P[(start + r) % len(P)], s_w, xq[name], xs[name], y[name])
+
     per_shape = {}
-    stream = torch.cuda.current_stream()
-    evs = {name: [(torch.cuda.Event(enable_timing=True),
-                   torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.kernel_reps)] for name in SHAPES}
-    for name in SHAPES:
-        tq.tq_act_quant(x[name], xq[name], xs[name])
-    torch.cuda.synchronize()
-    torch.cuda._sleep(spin)
-    for r in range(args.kernel_reps):        # same order and pool walk as a step
-        for name in SHAPES:
-            a, b = evs[name][r]
-            a.record(stream)
-            tq.tq_gemv(pool[r % n_sets][name], s_w, xq[name], xs[name], y[name])
-            b.record(stream)
-    torch.cuda.synchronize()
     for name, (N, K) in SHAPES.items():
-        times = [a.elapsed_time(b) * 1e3 for a, b in evs[name]]   # us
-        mean_us = float(np.mean(times))
+        tq.tq_act_quant(x[name], xq[name], xs[name])
+        nP = len(pools[name])
+        gs = [timer.graph(lambda name=name, s=s: gemv_loop(name, s))
+              for s in range(0, nP, max(1, nP // 4))][:4]
+        us = timer.time_graphs(gs, 8) * 1e3 / R
         per_shape[name] = {
-            "N": N, "K": K, "us_mean": round(mean_us, 3),
-            "us_median": round(float(np.median(times)), 3),
-            "weight_GBs": round(weight_bytes(N, K) / mean_us / 1e3, 1),
-            "pct_hbm_peak": round(100 * weight_bytes(N, K) / mean_us / 1e3 / HBM_PEAK_GBS, 1),
+            "N": N, "K": K, "us_per_launch": round(us, 3),
+            "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * weight_bytes(N, K) / us / 1e3 / HBM_PEAK_GBS, 1),
+            "algo_GBs": round(algo_bytes(N, K) / us / 1e3, 1),
         }
-        log(f"{name}: {per_shape[name]}")
+        log(f"gemv {name}: {per_shape[name]}")
 
-    dom_bytes = sum(algo_bytes(*SHAPES[n]) for n in DOMINANT)
-    dom_us = sum(per_shape[n]["us_mean"] for n in DOMINANT)
-    achieved = dom_bytes / dom_us / 1e3  # GB/s
-    traffic = read_traffic()
+    dN, dK = SHAPES[DOMINANT]
+    dom_us = per_shape[DOMINANT]["us_per_launch"]
+    achieved = algo_bytes(dN, dK) / dom_us / 1e3
+
+    rows = {}
+    if not args.no_rows:
+        rows = measure_rows(torch, tq, workloads, timer, dev, R, per_shape)
 
     cpu = None if args.no_cpu else cpu_baseline()
 
@@ -258,27 +289,182 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "ternary GEMV at M=1 over [N,K] = [2560,6912], [28672,8192], "
-                        "[8192,28672]; each shape act_quant(bf16) + gemv per step",
+            "workload": ("ternary GEMV at M=1, [N,K] = [2560,6912] (2B-4T down), "
+                         "[8192,28672] and [28672,8192] (70B-class, both "
+                         "orientations); per shape act_quant(bf16) + gemv per step"),
             "weight_bytes_per_step": step_wbytes,
-            "pool_sets": n_sets,
-            "pool_bytes": n_sets * set_bytes,
+            "pool_copies_per_shape": {k: len(v) for k, v in pools.items()},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_m1_kernel (70B-class shapes)",
+            "kernel": f"gemv_reg_kernel, tq_gemv [N,K]=[{dN},{dK}]",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": read_traffic(),
+            "us_per_launch": dom_us,
+            "bytes_per_launch": algo_bytes(dN, dK),
         },
         "per_shape": per_shape,
+        "rows": rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def counters_run(torch, tq, workloads, dev):
+    """Dispatches for the HBM-traffic counters: a plain device-to-device copy
+    of 256 MiB (calibration: its FETCH_SIZE and WRITE_SIZE should each read
+    256 MiB), then the dominant GEMV over 4 distinct weight copies."""
+    import numpy as np
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    N, K = SHAPES[DOMINANT]
+    P = []
+    for c in range(4):
+        w = workloads.ternary_codes_torch(N, K, seed=4242 + c, device=dev)
+        P.append(tq.tq_pack(w))
+        del w
+    xb = workloads.activations_bf16(1, K, seed=4243)
+    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, s = tq.tq_act_quant(xt)
+    yy = torch.empty(N, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for r in range(8):
+        tq.tq_gemv(P[r % 4], 0.02, q, s, yy)
+    torch.cuda.synchronize()
+    log("counters run done")
+
+
+def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
+    """Every hot-path row, graph-timed over cache-defeating pools."""
+    import numpy as np
+    from bit_gemv_tq_amd.chain import DecodeChain, Layer
+
+    rows = {}
+
+    def pool_of(N, K, min_bytes, seed0):
+        copies = max(4, -(-min_bytes // weight_bytes(N, K)))
+        out = []
+        for c in range(copies):
+            w = workloads.ternary_codes_torch(N, K, seed=seed0 + c, device=dev)
+            out.append(tq.tq_pack(w))
+            del w
+        return out
+
+    def loop_us(fn, nP, reps=8):
+        gs = [timer.graph(lambda s=s: fn(s)) for s in range(0, nP, max(1, nP // 4))][:4]
+        return timer.time_graphs(gs, reps) * 1e3 / R
+
+    # a1: act_quant on bf16 rows (input cache-resident: it is reused)
+    aq = {}
+    for K in (2560, 6912, 8192, 28672):
+        xb = workloads.activations_bf16(1, K, seed=K)
+        xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        q = torch.empty(K, dtype=torch.int8, device=dev)
+        s = torch.empty(1, dtype=torch.float32, device=dev)
+
+        def f(_, xt=xt, q=q, s=s):
+            for _r in range(R):
+                tq.tq_act_quant(xt, q, s)
+        aq[K] = round(loop_us(f, 1), 3)
+    rows["act_quant_us_per_launch_M1"] = aq
+    log(f"act_quant: {aq}")
+
+    # a2/a3 at the 2B-4T q_proj shape [2560, 2560] (the single-GEMV case)
+    N, K = workloads.HIDDEN, workloads.HIDDEN
+    P = pool_of(N, K, 640 << 20, 90000)
+    xb = workloads.activations_bf16(1, K, seed=90)
+    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, s = tq.tq_act_quant(xt)
+    yq = torch.empty(N, dtype=torch.float32, device=dev)
+
+    def fq(st):
+        for r in range(R):
+            tq.tq_gemv(P[(st + r) % len(P)], 0.02, q, s, yq)
+    us = loop_us(fq, len(P))
+    rows["gemv_q_proj_2560x2560"] = {
+        "us_per_launch": round(us, 3),
+        "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1)}
+    log(f"gemv q_proj: {rows['gemv_q_proj_2560x2560']}")
+    del P
+
+    # a4: fused gate/up + relu^2, M = 1 (2B-4T MLP)
+    N, K = workloads.INTERMEDIATE, workloads.HIDDEN
+    pg = pool_of(N, K, 320 << 20, 91000)
+    pu = pool_of(N, K, 320 << 20, 92000)
+    xb = workloads.activations_bf16(1, K, seed=93)
+    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, s = tq.tq_act_quant(xt)
+    h = torch.empty(N, dtype=torch.float32, device=dev)
+
+    def fg(st):
+        for r in range(R):
+            i = (st + r) % len(pg)
+            tq.tq_gate_up_relu2(pg[i], 0.024, pu[i], 0.025, q, s, h)
+    us = loop_us(fg, len(pg))
+    rows["gate_up_relu2_M1_6912x2560"] = {
+        "us_per_launch": round(us, 3),
+        "weight_GBs": round(2 * weight_bytes(N, K) / us / 1e3, 1)}
+    log(f"gate_up: {rows['gate_up_relu2_M1_6912x2560']}")
+    del pg, pu
+
+    # a5: small-batch GEMM on the int8 matrix cores
+    gemm = {}
+    for (N, K) in workloads.GEMM_SMALL_SHAPES:
+        P = pool_of(N, K, 640 << 20, 94000 + N)
+        for M in workloads.GEMM_SMALL_M:
+            xb = workloads.activations_bf16(M, K, seed=95 + M)
+            xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev).reshape(M, K)
+            q, s = tq.tq_act_quant(xt)
+            yy = torch.empty(M, N, dtype=torch.float32, device=dev)
+
+            def fm(st, P=P, q=q, s=s, yy=yy):
+                for r in range(R):
+                    tq.tq_gemm_small(P[(st + r) % len(P)], 0.02, q, s, yy)
+            us = loop_us(fm, len(P))
+            ops = 2.0 * M * N * K
+            gemm[f"M{M}_{N}x{K}"] = {
+                "us_per_launch": round(us, 3),
+                "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1),
+                "int8_TOPS": round(ops / us / 1e6, 2),
+                "mfma_frac": round(ops / us / 1e6 / INT8_MFMA_PEAK_TOPS, 4)}
+            log(f"gemm_small M={M} {N}x{K}: {gemm[f'M{M}_{N}x{K}']}")
+        del P
+    rows["gemm_small"] = gemm
+
+    # a6: the 30-layer decode-step chain (2B-4T layers, M = 1), one graph
+    layers = []
+    for l in range(workloads.CHAIN_LAYERS):
+        packed, scale = {}, {}
+        for name, (N, K) in workloads.LAYER_2B4T.items():
+            t = workloads.TENSOR_INDEX[name]
+            w = workloads.ternary_codes_torch(N, K, seed=workloads.seed_for(2, t, l), device=dev)
+            packed[name] = tq.tq_pack(w)
+            scale[name] = workloads.tensor_scale(t)
+            del w
+        layers.append(Layer(packed, scale))
+    chain = DecodeChain(layers, dev)
+    h0b = workloads.activations_bf16(1, workloads.HIDDEN, seed=97, outliers=True)
+    h0 = torch.from_numpy(h0b.view(np.int16)).view(torch.bfloat16).to(dev)[0]
+    g = timer.graph(lambda: chain.step(h0))
+    ms = timer.time_graphs([g], 20)
+    layer_bytes = sum(weight_bytes(*s) for s in workloads.LAYER_2B4T.values())
+    total = layer_bytes * workloads.CHAIN_LAYERS
+    rows["decode_chain_30x2b4t"] = {
+        "us_per_token": round(ms * 1e3, 2),
+        "tokens_per_s": round(1e3 / ms, 1),
+        "weight_GBs": round(total / (ms * 1e-3) / 1e9, 1),
+        "launches_per_token": 10 * workloads.CHAIN_LAYERS}
+    log(f"chain: {rows['decode_chain_30x2b4t']}")
+    return rows
 
 
 if __name__ == "__main__":

@@ -53,7 +53,8 @@ __device__ __forceinline__ uint32_t quant4(const float *v, float inv) {
   return out;
 }
 
-// One block per activation row.
+// Two passes (absmax, then quantize) for rows longer than the register
+// kernel holds; one block per activation row.
 template <bool kBf16>
 __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(
     const void *__restrict__ x, int64_t K, int8_t *__restrict__ q,
@@ -96,6 +97,71 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(
   if (threadIdx.x == 0) s_x[m] = ap / 127.0f;
 }
 
+// Single pass for K <= 32768: each thread keeps its PPT pieces (16 values
+// each) in registers between the absmax reduction and the quantization, so
+// the row is read once.
+constexpr int kAqRegThreads = 1024;
+
+template <bool kBf16, int PPT>
+__global__ __launch_bounds__(kAqRegThreads) void act_quant_reg_kernel(
+    const void *__restrict__ x, int64_t K, int8_t *__restrict__ q,
+    float *__restrict__ s_x) {
+  __shared__ float wave_max_lds[kAqRegThreads / kWave];
+  const int64_t m = blockIdx.x;
+  const int kp = (int)(K / 16);
+  const size_t elem = kBf16 ? 2 : 4;
+  const void *xr = reinterpret_cast<const char *>(x) + (size_t)(m * K) * elem;
+  float v[PPT][16];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = threadIdx.x + i * kAqRegThreads;
+    if (p < kp) {
+      load16<kBf16>(xr, p, v[i]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(v[i][e]));
+    }
+  }
+  a = wave_max(a);
+  if ((threadIdx.x & (kWave - 1)) == 0) wave_max_lds[threadIdx.x / kWave] = a;
+  __syncthreads();
+  a = wave_max_lds[0];
+#pragma unroll
+  for (int w = 1; w < kAqRegThreads / kWave; ++w) a = fmaxf(a, wave_max_lds[w]);
+
+  const float ap = a > 1e-5f ? a : 1e-5f;
+  const float inv = 127.0f / ap;  // correctly rounded fp32 division
+  uint4 *qr = reinterpret_cast<uint4 *>(q + m * K);
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = threadIdx.x + i * kAqRegThreads;
+    if (p < kp) {
+      uint4 o;
+      o.x = quant4(v[i] + 0, inv);
+      o.y = quant4(v[i] + 4, inv);
+      o.z = quant4(v[i] + 8, inv);
+      o.w = quant4(v[i] + 12, inv);
+      qr[p] = o;
+    }
+  }
+  if (threadIdx.x == 0) s_x[m] = ap / 127.0f;
+}
+
+template <bool kBf16>
+tq_status launch_act_quant(const void *x, int64_t M, int64_t K, int8_t *xq,
+                           float *x_scale, hipStream_t stream) {
+  const int64_t kp = K / 16;
+  const dim3 grid((unsigned)M);
+  if (kp <= kAqRegThreads)
+    return launch(act_quant_reg_kernel<kBf16, 1>, grid, dim3(kAqRegThreads), 0,
+                  stream, x, K, xq, x_scale);
+  if (kp <= 2 * kAqRegThreads)
+    return launch(act_quant_reg_kernel<kBf16, 2>, grid, dim3(kAqRegThreads), 0,
+                  stream, x, K, xq, x_scale);
+  return launch(act_quant_kernel<kBf16>, grid, dim3(kAqThreads), 0, stream, x,
+                K, xq, x_scale);
+}
+
 }  // namespace
 }  // namespace tq
 
@@ -112,9 +178,7 @@ extern "C" tq_status tq_act_quant(const void *x, tq_dtype xt, int64_t M,
     return TQ_ERR_ALIGN;
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
-  if (xt == TQ_BF16)
-    return launch(act_quant_kernel<true>, dim3((unsigned)M), dim3(kAqThreads),
-                  0, stream, x, K, xq, x_scale);
-  return launch(act_quant_kernel<false>, dim3((unsigned)M), dim3(kAqThreads),
-                0, stream, x, K, xq, x_scale);
+  return xt == TQ_BF16
+             ? launch_act_quant<true>(x, M, K, xq, x_scale, stream)
+             : launch_act_quant<false>(x, M, K, xq, x_scale, stream);
 }

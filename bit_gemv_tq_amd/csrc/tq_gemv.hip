@@ -1,5 +1,5 @@
 // tq_gemv.hip -- the ternary matrix-vector product at M = 1 (tq_gemv) and
-// the fused gate/up + squared-ReLU projection at M = 1 (tq_gate_up_relu2).
+// the M = 1 dispatch of the fused gate/up + squared-ReLU projection.
 //
 // Page "the full arc: how the 1bit.systems ternary stack got from broken to
 // 76.7 tok/s", TL;DR: a hand-tuned ternary GEMV running close to the memory-
@@ -8,16 +8,15 @@
 // skip.  Page "Feature request: BitNet 1.58-bit ternary inference on ROCm
 // (gfx1151)", section "Architecture": the MLP gate is relu_squared.
 //
-// gfx950 design (the pages' own kernel targets a wave32 iGPU and is not
-// followed): the decode GEMV is bound by HBM, so the kernel streams the
-// packed weights once with coalesced 16-byte non-temporal loads, keeps the
-// int8 activation row in LDS (staged once per block), turns each 16-byte
-// piece into 16 v_dot4_i32_i8 on offset codes (see tq_device.h: mask, no
-// multiply per weight), and reduces each row's partial sums across its lane
-// group with DPP.  A lane group of LPR lanes (16, 32 or 64) owns ROWS packed
-// rows at a time (4*ROWS outputs) and walks K in strides of 16*LPR bytes,
-// UNR pieces per lane in flight.
+// Two kernels.  For 1 <= K <= 32768 (every decode shape) the register-
+// resident kernel of tq_gemv_reg.h runs: activations staged once per block
+// and held in VGPRs, the packed weights streamed once with 16-byte
+// non-temporal loads.  For K == 0 and K > 32768 the kernel below keeps the
+// int8 activation row in LDS (dynamic, up to 128 KiB) and reads it per
+// 16-byte piece: lane groups of LPR lanes own ROWS packed rows at a time and
+// walk K in strides of 16*LPR bytes, UNR pieces per lane in flight.
 #include "tq_device.h"
+#include "tq_gemv_reg.h"
 #include "tq_host.h"
 
 namespace tq {
@@ -144,10 +143,8 @@ struct GemvPlan {
   int blocks;
 };
 
-GemvPlan plan_gemv(int64_t n4, int64_t kp, int num_cus, int nm) {
-  GemvPlan pl;
-  // Widest lane group that divides the row into whole 16-byte pieces per
-  // lane; rows of an odd number of pieces take masked tails.
+GemvPlan plan_gemv_lds(int64_t n4, int64_t kp, int num_cus, int nm) {
+  GemvPlan pl{};
   if (kp % 64 == 0) pl.lpr = 64;
   else if (kp % 32 == 0) pl.lpr = 32;
   else if (kp % 16 == 0) pl.lpr = 16;
@@ -156,7 +153,6 @@ GemvPlan plan_gemv(int64_t n4, int64_t kp, int num_cus, int nm) {
   pl.unr = 4;
   const int64_t groups = kGemvThreads / pl.lpr;
   const int64_t batches = (n4 + pl.rows - 1) / pl.rows;
-  // Residency: LDS holds K bytes per block; aim for <= 8 blocks per CU.
   const int64_t k_bytes = kp * 16;
   int64_t per_cu = k_bytes > 0 ? (160 * 1024) / (k_bytes + 64) : 8;
   if (per_cu > 8) per_cu = 8;
@@ -170,8 +166,8 @@ GemvPlan plan_gemv(int64_t n4, int64_t kp, int num_cus, int nm) {
 }
 
 template <bool kGate>
-tq_status launch_gemv(const GemvPlan &pl, const GemvArgs &a, size_t lds,
-                      hipStream_t s) {
+tq_status launch_gemv_lds(const GemvPlan &pl, const GemvArgs &a, size_t lds,
+                          hipStream_t s) {
   const dim3 grid(pl.blocks), block(kGemvThreads);
 #define TQ_GEMV_CASE(L, R, U)                                              \
   if (pl.lpr == L && pl.rows == R && pl.unr == U) {                        \
@@ -192,6 +188,41 @@ tq_status launch_gemv(const GemvPlan &pl, const GemvArgs &a, size_t lds,
 
 }  // namespace
 
+// Register-path plan (from launch-shape sweeps on MI355X): the narrowest
+// team that keeps at most 8 pieces per lane; 64-lane teams when that would
+// leave the chip short of busy lanes (small N).  Persistent blocks, about
+// 3 per CU (2 for the two-stream gate kernel).  Grids that give every team
+// exactly the same number of rows measured slower (all waves reach their
+// reductions at once), so the grid is not trimmed to a balanced count.
+RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate) {
+  RegPlan pl{};
+  int lpr = 16;
+  while ((kp + lpr - 1) / lpr > 8) lpr *= 2;
+  const int64_t want_lanes = (int64_t)num_cus * 16 * kWave;
+  if (lpr < 64 && n4 * lpr < want_lanes) lpr = 64;
+  pl.lpr = lpr;
+  pl.np = (int)((kp + lpr - 1) / lpr);
+  pl.exact = (int64_t)pl.np * lpr == kp;
+  const int64_t teams = kRegThreads / lpr;
+  int64_t blocks = (n4 + teams - 1) / teams;
+  const int64_t cap = (int64_t)num_cus * (gate ? 2 : 3);
+  if (blocks > cap) blocks = cap;
+  pl.blocks = (int)(blocks < 1 ? 1 : blocks);
+  return pl;
+}
+
+tq_status launch_gemv_reg(const RegPlan &pl, bool gate, const RegArgs &a,
+                          hipStream_t s) {
+  switch (pl.lpr) {
+    case 16: return launch_reg<16>(pl, gate, a, s);
+    case 32: return launch_reg<32>(pl, gate, a, s);
+    case 64: return launch_reg<64>(pl, gate, a, s);
+    case 128: return launch_reg<128>(pl, gate, a, s);
+    case 256: return launch_reg<256>(pl, gate, a, s);
+  }
+  return TQ_ERR_LAUNCH;
+}
+
 // Shared by tq_gemv and the M = 1 branch of tq_gate_up_relu2.
 tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
                   const int8_t *xq, const float *x_scale, int64_t N, int64_t K,
@@ -199,6 +230,13 @@ tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
   const bool gate = p1 != nullptr;
+  const int64_t n4 = N / 4, kp = K / 16;
+  if (kp >= 1 && kp <= kRegMaxPieces) {
+    RegArgs a{p0, p1, s0, s1, xq, x_scale, (int)n4, (int)kp, y, acc0, acc1};
+    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate), gate, a,
+                           stream);
+  }
+  // K == 0 or K > 32768: activations read from LDS per piece.
   GemvArgs a;
   a.p0 = p0;
   a.p1 = p1;
@@ -206,15 +244,15 @@ tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
   a.s1 = s1;
   a.xq = xq;
   a.x_scale = x_scale;
-  a.n4 = (int)(N / 4);
-  a.kp = (int)(K / 16);
+  a.n4 = (int)n4;
+  a.kp = (int)kp;
   a.y = y;
   a.acc0 = acc0;
   a.acc1 = acc1;
-  const GemvPlan pl = plan_gemv(a.n4, a.kp, dev.num_cus, gate ? 2 : 1);
+  const GemvPlan pl = plan_gemv_lds(n4, kp, dev.num_cus, gate ? 2 : 1);
   const size_t lds = (size_t)K;
-  return gate ? launch_gemv<true>(pl, a, lds, stream)
-              : launch_gemv<false>(pl, a, lds, stream);
+  return gate ? launch_gemv_lds<true>(pl, a, lds, stream)
+              : launch_gemv_lds<false>(pl, a, lds, stream);
 }
 
 }  // namespace tq

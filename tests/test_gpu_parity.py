@@ -142,9 +142,13 @@ def test_act_quant_scale_sweep(env):
 
 
 # ------------------------------------------------------------------ gemv
+# Covers: 16..256-lane teams, 1..8 pieces per lane with and without a ragged
+# last piece, cross-wave team reductions, persistent blocks walking several
+# rows, the largest register-path K (32768) and the LDS kernel just above it.
 GEMV_SHAPES = [(4, 16), (8, 32), (12, 48), (100, 1008), (36, 2064), (260, 400),
                (2560, 2560), (640, 2560), (6912, 2560), (2560, 6912),
-               (4, 131072), (2052, 16)]
+               (4, 131072), (2052, 16), (8, 32768), (4, 32784), (28, 16384),
+               (1024, 4608), (40000, 64), (3076, 1552)]
 
 
 def run_gemv(env, N, K, seed, s_w=np.float32(0.02)):
@@ -201,6 +205,7 @@ def test_gemv_zero_k_and_empty(env):
 
 # ------------------------------------------------------------------ gate/up
 @pytest.mark.parametrize("M,N,K", [(1, 6912, 2560), (1, 20, 48), (1, 100, 1008),
+                                   (1, 256, 28672), (1, 8, 40000), (1, 1028, 4608),
                                    (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560)])
 def test_gate_up_relu2(env, M, N, K):
     torch, tq, oracle = env
