@@ -28,7 +28,8 @@ STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN",
           4: "TQ_ERR_DTYPE", 5: "TQ_ERR_DEVICE", 6: "TQ_ERR_LAUNCH"}
 
 EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
-           "tq_gate_up_relu2", "tq_status_string")
+           "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
+           "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -51,6 +52,9 @@ def _load() -> ctypes.CDLL:
         "tq_gemv": [p, f32, p, p, i64, i64, p, p, p],
         "tq_gemm_small": [p, f32, p, p, i64, i64, i64, p, p, p],
         "tq_gate_up_relu2": [p, f32, p, f32, p, p, i64, i64, i64, p, p, p, p],
+        "tq_quant_gemv": [p, i32, p, f32, i64, i64, p, p, p, p, p, p],
+        "tq_quant_gate_up_relu2": [p, i32, p, f32, p, f32, i64, i64, p, p, p,
+                                   p, p, p, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -211,4 +215,72 @@ def tq_gate_up_relu2(packed_gate, s_gate, packed_up, s_up, xq, x_scale,
         _ptr(packed_gate), float(s_gate), _ptr(packed_up), float(s_up),
         _ptr(xq2), _ptr(x_scale), M, N, K, _ptr(h), _ptr(acc_gate),
         _ptr(acc_up), _stream(stream)))
+    return h
+
+
+def _raw_row(x):
+    torch = _torch()
+    if x.dtype == torch.bfloat16:
+        xt = TQ_BF16
+    elif x.dtype == torch.float32:
+        xt = TQ_F32
+    else:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    _need(x, "x", x.dtype)
+    return xt
+
+
+def tq_quant_gemv(x, packed, w_scale, y=None, acc=None, xq=None, x_scale=None,
+                  y_scale=None, stream=None):
+    """act_quant + gemv at M = 1 in one launch.  x: bf16/fp32 [K].  Returns
+    y; the quantized row and its scale land in xq / x_scale (allocated when
+    not given).  y_scale: optional fp32 [1] used in the rescale instead of
+    the row's own s_x."""
+    torch = _torch()
+    xt = _raw_row(x)
+    _need(packed, "packed", torch.uint8, x.device)
+    dev = packed.device
+    N, K = packed.shape[0] * 4, packed.shape[1]
+    if x.numel() != K:
+        raise ValueError(f"x has {x.numel()} elements, need K={K}")
+    y = _out(y, "y", (N,), torch.float32, dev)
+    if acc is not None:
+        acc = _out(acc, "acc", (N,), torch.int32, dev)
+    xq = _out(xq, "xq", (K,), torch.int8, dev)
+    x_scale = _out(x_scale, "x_scale", (1,), torch.float32, dev)
+    if y_scale is not None:
+        _need(y_scale, "y_scale", torch.float32, dev)
+    _check("tq_quant_gemv", lib.tq_quant_gemv(
+        _ptr(x), xt, _ptr(packed), float(w_scale), N, K, _ptr(y), _ptr(acc),
+        _ptr(xq), _ptr(x_scale), _ptr(y_scale), _stream(stream)))
+    return y
+
+
+def tq_quant_gate_up_relu2(x, packed_gate, s_gate, packed_up, s_up, h=None,
+                           acc_gate=None, acc_up=None, xq=None, x_scale=None,
+                           y_scale=None, stream=None):
+    """act_quant + gate/up + relu^2 at M = 1 in one launch.  Returns h."""
+    torch = _torch()
+    xt = _raw_row(x)
+    _need(packed_gate, "packed_gate", torch.uint8, x.device)
+    dev = packed_gate.device
+    _need(packed_up, "packed_up", torch.uint8, dev)
+    if packed_up.shape != packed_gate.shape:
+        raise ValueError("packed_gate and packed_up shapes differ")
+    N, K = packed_gate.shape[0] * 4, packed_gate.shape[1]
+    if x.numel() != K:
+        raise ValueError(f"x has {x.numel()} elements, need K={K}")
+    h = _out(h, "h", (N,), torch.float32, dev)
+    if acc_gate is not None:
+        acc_gate = _out(acc_gate, "acc_gate", (N,), torch.int32, dev)
+    if acc_up is not None:
+        acc_up = _out(acc_up, "acc_up", (N,), torch.int32, dev)
+    xq = _out(xq, "xq", (K,), torch.int8, dev)
+    x_scale = _out(x_scale, "x_scale", (1,), torch.float32, dev)
+    if y_scale is not None:
+        _need(y_scale, "y_scale", torch.float32, dev)
+    _check("tq_quant_gate_up_relu2", lib.tq_quant_gate_up_relu2(
+        _ptr(x), xt, _ptr(packed_gate), float(s_gate), _ptr(packed_up),
+        float(s_up), N, K, _ptr(h), _ptr(acc_gate), _ptr(acc_up), _ptr(xq),
+        _ptr(x_scale), _ptr(y_scale), _stream(stream)))
     return h

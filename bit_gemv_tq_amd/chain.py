@@ -22,7 +22,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import tq_act_quant, tq_gate_up_relu2, tq_gemv
+from . import (tq_act_quant, tq_gate_up_relu2, tq_gemv, tq_quant_gate_up_relu2,
+               tq_quant_gemv)
 
 PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -41,9 +42,15 @@ class Layer:
 
 
 class DecodeChain:
-    """Preallocated buffers and the launch sequence of one decode step."""
+    """Preallocated buffers and the launch sequence of one decode step.
 
-    def __init__(self, layers, device):
+    fused=False: ten launches per layer (separate act-quant launches);
+    fused=True: six, each projection quantizing its own input in the GEMV
+    prologue (tq_quant_gemv / tq_quant_gate_up_relu2).  Both give
+    bit-identical stages."""
+
+    def __init__(self, layers, device, fused=False):
+        self.fused = fused
         import torch
         self.layers = layers
         self.device = device
@@ -63,6 +70,9 @@ class DecodeChain:
         self.h = [e(H), e(H)]   # ping-pong layer outputs
 
     def layer(self, L: Layer, h_in, h_out, record=None, stream=None):
+        if self.fused:
+            self.layer_fused(L, h_in, h_out, record, stream)
+            return
         u = self.unit
         tq_act_quant(h_in, self.q8_in, self.s_in, stream=stream)
         tq_gemv(L.packed["q"], L.scale["q"], self.q8_in, u, self.q, stream=stream)
@@ -76,6 +86,24 @@ class DecodeChain:
         tq_act_quant(self.f, self.q8_d, self.s_d, stream=stream)
         tq_gemv(L.packed["down"], L.scale["down"], self.q8_d, u, h_out,
                 stream=stream)
+        if record is not None:
+            record.append({name: getattr(self, name).clone() for name in
+                           ("q8_in", "s_in", "q", "k", "v", "q8_o", "o", "q8_f",
+                            "f", "q8_d")} | {"h": h_out.clone()})
+
+    def layer_fused(self, L: Layer, h_in, h_out, record=None, stream=None):
+        u, st = self.unit, stream
+        for name, out in (("q", self.q), ("k", self.k), ("v", self.v)):
+            tq_quant_gemv(h_in, L.packed[name], L.scale[name], out,
+                          xq=self.q8_in, x_scale=self.s_in, y_scale=u, stream=st)
+        tq_quant_gemv(self.q, L.packed["o"], L.scale["o"], self.o,
+                      xq=self.q8_o, x_scale=self.s_o, y_scale=u, stream=st)
+        tq_quant_gate_up_relu2(self.o, L.packed["gate"], L.scale["gate"],
+                               L.packed["up"], L.scale["up"], self.f,
+                               xq=self.q8_f, x_scale=self.s_f, y_scale=u,
+                               stream=st)
+        tq_quant_gemv(self.f, L.packed["down"], L.scale["down"], h_out,
+                      xq=self.q8_d, x_scale=self.s_d, y_scale=u, stream=st)
         if record is not None:
             record.append({name: getattr(self, name).clone() for name in
                            ("q8_in", "s_in", "q", "k", "v", "q8_o", "o", "q8_f",

@@ -13,46 +13,6 @@ namespace {
 
 constexpr int kAqThreads = 512;
 
-// 16 consecutive activations of one row, widened exactly to fp32.
-template <bool kBf16>
-__device__ __forceinline__ void load16(const void *x, int64_t piece,
-                                       float (&v)[16]) {
-  if constexpr (kBf16) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(x) + 2 * piece;
-    const uint4 h[2] = {p[0], p[1]};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t d[4] = {h[i].x, h[i].y, h[i].z, h[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
-      }
-    }
-  } else {
-    const float4 *p = reinterpret_cast<const float4 *>(x) + 4 * piece;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 f = p[i];
-      v[4 * i] = f.x;
-      v[4 * i + 1] = f.y;
-      v[4 * i + 2] = f.z;
-      v[4 * i + 3] = f.w;
-    }
-  }
-}
-
-__device__ __forceinline__ uint32_t quant4(const float *v, float inv) {
-  uint32_t out = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float r = __builtin_rintf(v[i] * inv);  // v_rndne_f32: ties to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    out |= ((uint32_t)(int)r & 0xffu) << (8 * i);
-  }
-  return out;
-}
-
 // Two passes (absmax, then quantize) for rows longer than the register
 // kernel holds; one block per activation row.
 template <bool kBf16>

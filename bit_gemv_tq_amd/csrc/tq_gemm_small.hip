@@ -8,16 +8,16 @@
 // requests at once, i.e. several activation rows per weight read.
 //
 // Mapping: v_mfma_i32_16x16x64_i8 computes D[16x16] += A[16x64] * B[64x16].
-// A = 16 packed weight rows of one plane (the codes w+1 in {0,1,2} are valid
-// int8), B = 16 activation rows.  Lane l loads 16 bytes of packed row
-// i0 + (l % 16) at k offset 16*(l / 16) of a 64-byte k step; that one load
-// gives the A operands of all four planes (4 output row blocks).  B is the
-// same 16-byte k block of activation row l % 16.  Because A and B take the
-// same k block per lane, the sum over k does not depend on how the matrix
-// core orders k inside its 64-wide step.  The waves of a block split the k
-// steps; partial tiles are summed in LDS with integer atomics (exact, order
-// free), and sum(q) per activation row, needed to remove the code offset,
-// is accumulated from the same B operands with v_dot4.
+// A = 16 packed weight rows of one plane, decoded to signed int8 {-1,0,+1}
+// with one v_perm_b32 byte lookup per dword; B = 16 activation rows.  Lane
+// l loads 16 bytes of packed row i0 + (l % 16) at k offset 16*(l / 16) of a
+// 64-byte k step; that one load gives the A operands of all four planes
+// (4 output row blocks).  B is the same 16-byte k block of activation row
+// l % 16.  Because A and B take the same k block per lane, the sum over k
+// does not depend on how the matrix core orders k inside its step.  The
+// eight waves of a block own contiguous k ranges and keep U k steps of loads
+// in flight; their partial tiles are summed in LDS with integer atomics
+// (exact, order free).
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -31,7 +31,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmWaves = 4;
+constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * kWave;
 
 struct GemmArgs {
@@ -44,24 +44,27 @@ struct GemmArgs {
   int32_t *acc0, *acc1;
 };
 
-__device__ __forceinline__ v4i plane_operand(const uint4 &w, int j) {
+// Plane j of a 16-byte piece as signed weights: codes {0,1,2} select the
+// bytes 0xFF, 0x00, 0x01 (-1, 0, +1) of a 4-byte table.
+__device__ __forceinline__ v4i signed_plane(const uint4 &w, int j) {
+  constexpr uint32_t kTable = 0x000100FFu;
   const int sh = 2 * j;
   v4i a;
-  a[0] = (int)((w.x >> sh) & 0x03030303u);
-  a[1] = (int)((w.y >> sh) & 0x03030303u);
-  a[2] = (int)((w.z >> sh) & 0x03030303u);
-  a[3] = (int)((w.w >> sh) & 0x03030303u);
+  a[0] = (int)__builtin_amdgcn_perm(0u, kTable, (w.x >> sh) & 0x03030303u);
+  a[1] = (int)__builtin_amdgcn_perm(0u, kTable, (w.y >> sh) & 0x03030303u);
+  a[2] = (int)__builtin_amdgcn_perm(0u, kTable, (w.z >> sh) & 0x03030303u);
+  a[3] = (int)__builtin_amdgcn_perm(0u, kTable, (w.w >> sh) & 0x03030303u);
   return a;
 }
 
-template <int MT, bool kGate>
+template <int MT, int U, bool kGate>
 __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
   constexpr int NM = kGate ? 2 : 1;
   constexpr int kTileInts = 64 * 4;               // one 16x16 int32 tile
   constexpr int kRed = NM * 4 * MT * kTileInts;   // all tiles of the block
-  __shared__ int red[kRed + 16 * MT];             // tiles, then sum(q)
+  __shared__ int red[kRed];
 
-  for (int t = threadIdx.x; t < kRed + 16 * MT; t += kGemmThreads) red[t] = 0;
+  for (int t = threadIdx.x; t < kRed; t += kGemmThreads) red[t] = 0;
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -71,50 +74,65 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
   const int kb = 16 * (lane >> 4);
   const int K = g.K;
   const int nsteps = (K + 63) / 64;
+  const int per = (nsteps + kGemmWaves - 1) / kGemmWaves;
+  const int s0 = min(wave * per, nsteps);
+  const int s1 = min(s0 + per, nsteps);
 
   const uint8_t *P[NM];
   P[0] = g.p0 + (size_t)prow * K;
   if constexpr (kGate) P[NM - 1] = g.p1 + (size_t)prow * K;
-
-  v4i acc[NM][4][MT];
-  int sq[MT];
+  const int8_t *Q[MT];
+  bool qrow_ok[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    sq[t] = 0;
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[m][j][t] = v4i{0, 0, 0, 0};
+    const int row = 16 * t + (lane & 15);
+    qrow_ok[t] = row < g.M;
+    Q[t] = g.xq + (size_t)min(row, g.M - 1) * K;
   }
 
-  for (int s = wave; s < nsteps; s += kGemmWaves) {
-    const int k = s * 64 + kb;
-    const bool ok = k < K;
-    uint4 w[NM];
+  v4i acc[NM][4][MT];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-      w[m] = ok ? load_stream16(reinterpret_cast<const uint4 *>(P[m] + k))
-                : make_uint4(0, 0, 0, 0);
-    v4i b[MT];
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int row = 16 * t + (lane & 15);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (ok && row < g.M)
-        v = *reinterpret_cast<const uint4 *>(g.xq + (size_t)row * K + k);
-      sq[t] = sum_bytes16(v, sq[t]);
-      b[t] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-    }
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+      for (int t = 0; t < MT; ++t) acc[m][j][t] = v4i{0, 0, 0, 0};
+
+  for (int s = s0; s < s1; s += U) {
+    // U k steps of loads in flight.  Slots past this wave's range (or past
+    // K) read an in-bounds piece and get a zero activation operand.
+    uint4 w[U][NM];
+    v4i b[U][MT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i a = plane_operand(w[m], j);
+    for (int u = 0; u < U; ++u) {
+      const int kk = (s + u) * 64 + kb;
+      const bool ok = s + u < s1 && kk < K;  // K % 64 may leave a ragged step
+      const int k = ok ? kk : 0;
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[m][j][t] =
-              __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[t], acc[m][j][t], 0, 0, 0);
+      for (int m = 0; m < NM; ++m)
+        w[u][m] = load_stream16(reinterpret_cast<const uint4 *>(P[m] + k));
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(Q[t] + k);
+        const bool use = ok && qrow_ok[t];
+        b[u][t] = use ? v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}
+                      : v4i{0, 0, 0, 0};
       }
+    }
+    // Keep all U steps of loads ahead of the first MFMA.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v4i a = signed_plane(w[u][m], j);
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[m][j][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[u][t],
+                                                                 acc[m][j][t], 0, 0, 0);
+        }
   }
 
   // Exact cross-wave reduction in LDS.
@@ -128,8 +146,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
         for (int i = 0; i < 4; ++i)
           atomicAdd(&red[((m * 4 + j) * MT + t) * kTileInts + lane * 4 + i],
                     acc[m][j][t][i]);
-#pragma unroll
-  for (int t = 0; t < MT; ++t) atomicAdd(&red[kRed + 16 * t + (lane & 15)], sq[t]);
   __syncthreads();
 
   // Epilogue.  Output tile layout of the 16x16 int32 result: lane l holds
@@ -142,7 +158,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
     const int c = lane & 15;
     const int m = 16 * t + c;
     if (m >= g.M) continue;
-    const int sumq = red[kRed + m];
     const float sx = g.x_scale[m];
     const float c0 = g.s0 * sx, c1 = g.s1 * sx;
 #pragma unroll
@@ -151,11 +166,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
       if (i0 + r >= g.n4) break;
       const size_t n = (size_t)j * g.n4 + i0 + r;
       const size_t o = (size_t)m * N + n;
-      const int v0 = red[((0 * 4 + j) * MT + t) * kTileInts + lane * 4 + i] - sumq;
+      const int v0 = red[((0 * 4 + j) * MT + t) * kTileInts + lane * 4 + i];
       if (g.acc0) g.acc0[o] = v0;
       if constexpr (kGate) {
-        const int v1 =
-            red[(((NM - 1) * 4 + j) * MT + t) * kTileInts + lane * 4 + i] - sumq;
+        const int v1 = red[(((NM - 1) * 4 + j) * MT + t) * kTileInts + lane * 4 + i];
         if (g.acc1) g.acc1[o] = v1;
         g.y[o] = relu2_gate(rescale(v0, c0), rescale(v1, c1));
       } else {
@@ -165,15 +179,34 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
   }
 }
 
+// k steps in flight per wave: the whole per-wave range when it is short,
+// fewer for larger M (the activation operands cost 4*MT VGPRs per step).
+template <int MT, bool kGate>
+tq_status launch_gemm_mt(const GemmArgs &a, hipStream_t s) {
+  const dim3 grid((a.n4 + 15) / 16), block(kGemmThreads);
+  const int nsteps = (a.K + 63) / 64;
+  const int per = (nsteps + kGemmWaves - 1) / kGemmWaves;
+  constexpr int kUMax = kGate ? (MT <= 1 ? 8 : (MT == 2 ? 4 : 2))
+                              : (MT <= 2 ? 8 : 4);
+  if constexpr (kUMax == 2) {
+    return launch(gemm_small_kernel<MT, 2, kGate>, grid, block, 0, s, a);
+  } else if constexpr (kUMax == 4) {
+    if (per <= 2) return launch(gemm_small_kernel<MT, 2, kGate>, grid, block, 0, s, a);
+    return launch(gemm_small_kernel<MT, 4, kGate>, grid, block, 0, s, a);
+  } else {
+    if (per <= 2) return launch(gemm_small_kernel<MT, 2, kGate>, grid, block, 0, s, a);
+    if (per <= 4) return launch(gemm_small_kernel<MT, 4, kGate>, grid, block, 0, s, a);
+    return launch(gemm_small_kernel<MT, 8, kGate>, grid, block, 0, s, a);
+  }
+}
+
 template <bool kGate>
 tq_status launch_gemm(int M, const GemmArgs &a, hipStream_t s) {
-  const dim3 grid((a.n4 + 15) / 16), block(kGemmThreads);
-  const int mt = (M + 15) / 16;
-  switch (mt) {
-    case 1: return launch(gemm_small_kernel<1, kGate>, grid, block, 0, s, a);
-    case 2: return launch(gemm_small_kernel<2, kGate>, grid, block, 0, s, a);
-    case 3: return launch(gemm_small_kernel<3, kGate>, grid, block, 0, s, a);
-    case 4: return launch(gemm_small_kernel<4, kGate>, grid, block, 0, s, a);
+  switch ((M + 15) / 16) {
+    case 1: return launch_gemm_mt<1, kGate>(a, s);
+    case 2: return launch_gemm_mt<2, kGate>(a, s);
+    case 3: return launch_gemm_mt<3, kGate>(a, s);
+    case 4: return launch_gemm_mt<4, kGate>(a, s);
   }
   return TQ_ERR_SHAPE;
 }

@@ -211,14 +211,14 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate) {
   return pl;
 }
 
-tq_status launch_gemv_reg(const RegPlan &pl, bool gate, const RegArgs &a,
-                          hipStream_t s) {
+tq_status launch_gemv_reg(const RegPlan &pl, bool gate, int xt,
+                          const RegArgs &a, hipStream_t s) {
   switch (pl.lpr) {
-    case 16: return launch_reg<16>(pl, gate, a, s);
-    case 32: return launch_reg<32>(pl, gate, a, s);
-    case 64: return launch_reg<64>(pl, gate, a, s);
-    case 128: return launch_reg<128>(pl, gate, a, s);
-    case 256: return launch_reg<256>(pl, gate, a, s);
+    case 16: return launch_reg<16>(pl, gate, xt, a, s);
+    case 32: return launch_reg<32>(pl, gate, xt, a, s);
+    case 64: return launch_reg<64>(pl, gate, xt, a, s);
+    case 128: return launch_reg<128>(pl, gate, xt, a, s);
+    case 256: return launch_reg<256>(pl, gate, xt, a, s);
   }
   return TQ_ERR_LAUNCH;
 }
@@ -232,9 +232,10 @@ tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
   const bool gate = p1 != nullptr;
   const int64_t n4 = N / 4, kp = K / 16;
   if (kp >= 1 && kp <= kRegMaxPieces) {
-    RegArgs a{p0, p1, s0, s1, xq, x_scale, (int)n4, (int)kp, y, acc0, acc1};
-    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate), gate, a,
-                           stream);
+    RegArgs a{p0,  p1,   s0,   s1,      xq,      x_scale, (int)n4, (int)kp,
+              y,   acc0, acc1, nullptr, nullptr, nullptr, nullptr};
+    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate), gate,
+                           kXInt8, a, stream);
   }
   // K == 0 or K > 32768: activations read from LDS per piece.
   GemvArgs a;
@@ -255,7 +256,78 @@ tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
               : launch_gemv_lds<false>(pl, a, lds, stream);
 }
 
+// Per-token quantization of a raw activation row fused into the GEMV
+// prologue (one launch); K == 0 or K > 32768 take two launches.
+tq_status quant_gemv_m1(const void *x, tq_dtype xt, const uint8_t *p0,
+                        float s0, const uint8_t *p1, float s1, int64_t N,
+                        int64_t K, float *y, int32_t *acc0, int32_t *acc1,
+                        int8_t *xq, float *x_scale, const float *y_scale,
+                        hipStream_t stream) {
+  DeviceInfo dev;
+  if (tq_status s = current_device(&dev)) return s;
+  const bool gate = p1 != nullptr;
+  const int64_t n4 = N / 4, kp = K / 16;
+  if (N > 0 && kp >= 1 && kp <= kRegMaxPieces) {
+    RegArgs a{p0, p1,   s0,   s1, nullptr, nullptr, (int)n4, (int)kp,
+              y,  acc0, acc1, x,  xq,      x_scale, y_scale};
+    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate), gate,
+                           xt == TQ_BF16 ? kXBf16 : kXF32, a, stream);
+  }
+  if (tq_status s = tq_act_quant(x, xt, 1, K, xq, x_scale, stream)) return s;
+  if (N == 0) return TQ_OK;
+  return gemv_m1(p0, s0, p1, s1, xq, y_scale ? y_scale : x_scale, N, K, y,
+                 acc0, acc1, stream);
+}
+
+tq_status check_quant_args(const void *x, tq_dtype xt, const uint8_t *p,
+                           int64_t N, int64_t K, const float *y,
+                           const int32_t *acc0, const int32_t *acc1,
+                           const int8_t *xq, const float *x_scale,
+                           const float *y_scale) {
+  if (xt != TQ_BF16 && xt != TQ_F32) return TQ_ERR_DTYPE;
+  if (tq_status s = check_nk(N, K)) return s;
+  if (!x_scale || (K > 0 && (!x || !xq)) || (N > 0 && !y) ||
+      (N > 0 && K > 0 && !p))
+    return TQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(p, 16) || !aligned(xq, 16) ||
+      !aligned(y, 4) || !aligned(acc0, 4) || !aligned(acc1, 4) ||
+      !aligned(x_scale, 4) || !aligned(y_scale, 4))
+    return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
 }  // namespace tq
+
+extern "C" tq_status tq_quant_gemv(const void *x, tq_dtype xt,
+                                   const uint8_t *packed, float w_scale,
+                                   int64_t N, int64_t K, float *y,
+                                   int32_t *acc, int8_t *xq, float *x_scale,
+                                   const float *y_scale, hipStream_t stream) {
+  using namespace tq;
+  if (tq_status s = check_quant_args(x, xt, packed, N, K, y, acc, nullptr, xq,
+                                     x_scale, y_scale))
+    return s;
+  return quant_gemv_m1(x, xt, packed, w_scale, nullptr, 0.0f, N, K, y, acc,
+                       nullptr, xq, x_scale, y_scale, stream);
+}
+
+extern "C" tq_status tq_quant_gate_up_relu2(
+    const void *x, tq_dtype xt, const uint8_t *packed_gate, float s_gate,
+    const uint8_t *packed_up, float s_up, int64_t N, int64_t K, float *h,
+    int32_t *acc_gate, int32_t *acc_up, int8_t *xq, float *x_scale,
+    const float *y_scale, hipStream_t stream) {
+  using namespace tq;
+  if (tq_status s = check_quant_args(x, xt, packed_gate, N, K, h, acc_gate,
+                                     acc_up, xq, x_scale, y_scale))
+    return s;
+  if (N > 0 && K > 0 && !packed_up) return TQ_ERR_NULL;
+  if (!aligned(packed_up, 16)) return TQ_ERR_ALIGN;
+  // The kernels tell the gated form by a non-null second stream; with K == 0
+  // both streams are empty, so any non-null stand-in keeps the gated path.
+  const uint8_t *pu = packed_up ? packed_up : reinterpret_cast<const uint8_t *>(x_scale);
+  return quant_gemv_m1(x, xt, packed_gate, s_gate, pu, s_up, N, K, h, acc_gate,
+                       acc_up, xq, x_scale, y_scale, stream);
+}
 
 extern "C" tq_status tq_gemv(const uint8_t *packed, float w_scale,
                              const int8_t *xq, const float *x_scale, int64_t N,

@@ -31,30 +31,61 @@ namespace tq {
 constexpr int kRegThreads = 256;
 constexpr int kRegMaxPieces = 2048;  // K <= 32768 bytes
 
+// Activation forms: kXInt8 = int8 row + scale given (tq_gemv); kXBf16 /
+// kXF32 = raw row, quantized in the prologue (tq_quant_gemv).
+constexpr int kXInt8 = 0, kXBf16 = 1, kXF32 = 2;
+
 struct RegArgs {
-  const uint8_t *p0;  // packed [N/4,K] (gate when kGate)
-  const uint8_t *p1;  // packed up (kGate only)
-  float s0, s1;       // weight scales
-  const int8_t *xq;   // [K]
-  const float *x_scale;
-  int n4;             // N/4
-  int kp;             // K/16
-  float *y;           // [N] (h when kGate)
-  int32_t *acc0;      // optional [N]
-  int32_t *acc1;      // optional [N] (kGate only)
+  const uint8_t *p0;     // packed [N/4,K] (gate when kGate)
+  const uint8_t *p1;     // packed up (kGate only)
+  float s0, s1;          // weight scales
+  const int8_t *xq;      // [K] int8 activations (kXInt8)
+  const float *x_scale;  // [1] their scale (kXInt8)
+  int n4;                // N/4
+  int kp;                // K/16
+  float *y;              // [N] (h when kGate)
+  int32_t *acc0;         // optional [N]
+  int32_t *acc1;         // optional [N] (kGate only)
+  const void *x;         // [K] raw bf16/fp32 row (kXBf16, kXF32)
+  int8_t *xq_out;        // [K] quantized row, written by block 0 (raw forms)
+  float *xs_out;         // [1] its scale s_x, written by block 0 (raw forms)
+  const float *y_scale;  // optional [1]: activation scale used in the
+                         // rescale instead of s_x (raw forms)
 };
 
-template <int LPR, int NP, bool EXACT, bool kGate>
-__global__ __launch_bounds__(kRegThreads) void gemv_reg_kernel(RegArgs g) {
+// 16 raw activations of one piece (VPP 16-byte words) widened to fp32.
+template <int XT>
+__device__ __forceinline__ void piece_floats(const u32x4 (&r)[XT == kXBf16 ? 2 : 4],
+                                             float (&f)[16]) {
+  if constexpr (XT == kXBf16) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[8 * i + 2 * j] = __uint_as_float(r[i][j] << 16);
+        f[8 * i + 2 * j + 1] = __uint_as_float(r[i][j] & 0xffff0000u);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[4 * i + j] = __uint_as_float(r[i][j]);
+  }
+}
+
+template <int LPR, int NP, bool EXACT, bool kGate, int XT, int BT = kRegThreads>
+__global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   constexpr int NM = kGate ? 2 : 1;
-  constexpr int G = kRegThreads / LPR;                // teams per block
+  constexpr int G = BT / LPR;                         // teams per block
   constexpr int GL = LPR < kWave ? LPR : kWave;       // DPP reduction width
   constexpr int WPT = LPR > kWave ? LPR / kWave : 1;  // waves per team
   constexpr int SPAN = NP * LPR;                      // pieces a team covers
-  constexpr int SP = (SPAN + kRegThreads - 1) / kRegThreads;  // staging loads
+  constexpr int SP = (SPAN + BT - 1) / BT;  // staging loads
   static_assert(NP >= 1 && SPAN <= kRegMaxPieces, "pieces per lane");
-  __shared__ u32x4 x_lds[SP * kRegThreads];  // padded: stores unconditional
-  __shared__ int red[2][kRegThreads / kWave][NM][4];
+  constexpr int VPP = XT == kXInt8 ? 1 : (XT == kXBf16 ? 2 : 4);  // words/piece
+  __shared__ u32x4 x_lds[SP * BT];  // padded: stores unconditional
+  __shared__ int red[2][BT / kWave][NM][4];
+  __shared__ float amax_lds[BT / kWave];
 
   const int kp = g.kp, n4 = g.n4;
   const int lane = threadIdx.x % LPR;
@@ -75,14 +106,17 @@ __global__ __launch_bounds__(kRegThreads) void gemv_reg_kernel(RegArgs g) {
     return EXACT ? p : min(p, kp - 1);
   };
 
-  // 1. Activation loads first (static count).
-  // (Native clang vectors: the compiler keeps these in VGPRs.)
-  const u32x4 *xg = reinterpret_cast<const u32x4 *>(g.xq);
-  u32x4 xs[SP];
+  // 1. Activation loads first (static count).  Thread i stages pieces
+  // i + s*256.  (Native clang vectors: the compiler keeps these in VGPRs.)
+  const u32x4 *xg = reinterpret_cast<const u32x4 *>(
+      XT == kXInt8 ? static_cast<const void *>(g.xq) : g.x);
+  u32x4 xs[SP][VPP];
 #pragma unroll
   for (int s = 0; s < SP; ++s) {
-    const int p = (int)threadIdx.x + s * kRegThreads;
-    xs[s] = xg[EXACT ? min(p, SPAN - 1) : min(p, kp - 1)];
+    const int p = (int)threadIdx.x + s * BT;
+    const int pc = EXACT ? min(p, SPAN - 1) : min(p, kp - 1);
+#pragma unroll
+    for (int v = 0; v < VPP; ++v) xs[s][v] = xg[pc * VPP + v];
   }
   // Keep the scheduler from sinking these loads below the weight loads.
   __builtin_amdgcn_sched_barrier(0);
@@ -101,9 +135,51 @@ __global__ __launch_bounds__(kRegThreads) void gemv_reg_kernel(RegArgs g) {
   issue(wa, rb0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. Stage x through LDS; keep this lane's pieces in VGPRs.
+  // 3. Stage x through LDS (quantizing a raw row first); keep this lane's
+  // pieces in VGPRs.
+  float sx;
+  if constexpr (XT == kXInt8) {
 #pragma unroll
-  for (int s = 0; s < SP; ++s) x_lds[threadIdx.x + s * kRegThreads] = xs[s];
+    for (int s = 0; s < SP; ++s) x_lds[threadIdx.x + s * BT] = xs[s][0];
+    sx = g.x_scale[0];
+  } else {
+    // Per-token absmax over the whole row (every block, redundantly), then
+    // q = clamp(rne(x * (127/a')), +-127) exactly as tq_act_quant.
+    float a = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      const int p = (int)threadIdx.x + s * BT;
+      if (p < kp) {
+        float f[16];
+        piece_floats<XT>(xs[s], f);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(f[e]));
+      }
+    }
+    a = wave_max(a);
+    if ((threadIdx.x & (kWave - 1)) == 0) amax_lds[wave] = a;
+    __syncthreads();
+    a = amax_lds[0];
+#pragma unroll
+    for (int w = 1; w < BT / kWave; ++w) a = fmaxf(a, amax_lds[w]);
+    const float ap = a > 1e-5f ? a : 1e-5f;
+    const float inv = 127.0f / ap;  // correctly rounded fp32 division
+    const float s_x = ap / 127.0f;
+    const bool writer = blockIdx.x == 0;
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      const int p = (int)threadIdx.x + s * BT;
+      float f[16];
+      piece_floats<XT>(xs[s], f);
+      const u32x4 q = {quant4(f + 0, inv), quant4(f + 4, inv),
+                       quant4(f + 8, inv), quant4(f + 12, inv)};
+      x_lds[threadIdx.x + s * BT] = q;
+      if (writer && p < kp)
+        reinterpret_cast<u32x4 *>(g.xq_out)[p] = q;
+    }
+    if (writer && threadIdx.x == 0) g.xs_out[0] = s_x;
+    sx = g.y_scale ? g.y_scale[0] : s_x;
+  }
   __syncthreads();
   uint4 xr[NP];
   int sq = 0;
@@ -118,7 +194,6 @@ __global__ __launch_bounds__(kRegThreads) void gemv_reg_kernel(RegArgs g) {
   // Per-plane accumulator start: -scale_j * (this lane's share of sum(q)).
   const int init[4] = {-sq, -4 * sq, -16 * sq, -16 * sq};
 
-  const float sx = g.x_scale[0];
   const float c0 = g.s0 * sx;
   const float c1 = g.s1 * sx;
 
@@ -197,35 +272,68 @@ struct RegPlan {
 };
 
 template <int LPR>
-tq_status launch_reg(const RegPlan &pl, bool gate, const RegArgs &a,
+tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
                      hipStream_t s);
 
-#define TQ_REG_KERNEL(LPR, NPV, GATE)                                          \
-  (pl.exact ? gemv_reg_kernel<LPR, NPV, true, GATE>                            \
-            : gemv_reg_kernel<LPR, NPV, false, GATE>)
+#define TQ_REG_KERNEL(LPR, NPV, GATE, XT)                                      \
+  (pl.exact ? gemv_reg_kernel<LPR, NPV, true, GATE, XT>                        \
+            : gemv_reg_kernel<LPR, NPV, false, GATE, XT>)
 
-#define TQ_REG_NP_CASES(LPR, GATE)                                             \
+#define TQ_REG_NP_CASES(LPR, GATE, XT)                                         \
   switch (pl.np) {                                                             \
-    case 1: return launch(TQ_REG_KERNEL(LPR, 1, GATE), grid, block, 0, s, a);  \
-    case 2: return launch(TQ_REG_KERNEL(LPR, 2, GATE), grid, block, 0, s, a);  \
-    case 3: return launch(TQ_REG_KERNEL(LPR, 3, GATE), grid, block, 0, s, a);  \
-    case 4: return launch(TQ_REG_KERNEL(LPR, 4, GATE), grid, block, 0, s, a);  \
-    case 5: return launch(TQ_REG_KERNEL(LPR, 5, GATE), grid, block, 0, s, a);  \
-    case 6: return launch(TQ_REG_KERNEL(LPR, 6, GATE), grid, block, 0, s, a);  \
-    case 7: return launch(TQ_REG_KERNEL(LPR, 7, GATE), grid, block, 0, s, a);  \
-    case 8: return launch(TQ_REG_KERNEL(LPR, 8, GATE), grid, block, 0, s, a);  \
+    case 1: return launch(TQ_REG_KERNEL(LPR, 1, GATE, XT), grid, block, 0, s, a); \
+    case 2: return launch(TQ_REG_KERNEL(LPR, 2, GATE, XT), grid, block, 0, s, a); \
+    case 3: return launch(TQ_REG_KERNEL(LPR, 3, GATE, XT), grid, block, 0, s, a); \
+    case 4: return launch(TQ_REG_KERNEL(LPR, 4, GATE, XT), grid, block, 0, s, a); \
+    case 5: return launch(TQ_REG_KERNEL(LPR, 5, GATE, XT), grid, block, 0, s, a); \
+    case 6: return launch(TQ_REG_KERNEL(LPR, 6, GATE, XT), grid, block, 0, s, a); \
+    case 7: return launch(TQ_REG_KERNEL(LPR, 7, GATE, XT), grid, block, 0, s, a); \
+    case 8: return launch(TQ_REG_KERNEL(LPR, 8, GATE, XT), grid, block, 0, s, a); \
   }                                                                            \
   return TQ_ERR_LAUNCH;
 
-#define TQ_DEFINE_LAUNCH_REG(LPR)                                              \
+#define TQ_REG_XT_CASES(LPR, GATE)                                             \
+  switch (xt) {                                                                \
+    case kXInt8: { TQ_REG_NP_CASES(LPR, GATE, kXInt8) }                        \
+    case kXBf16: { TQ_REG_NP_CASES(LPR, GATE, kXBf16) }                        \
+    case kXF32: { TQ_REG_NP_CASES(LPR, GATE, kXF32) }                          \
+  }                                                                            \
+  return TQ_ERR_DTYPE;
+
+#define TQ_DEFINE_LAUNCH_REG(LPR, GATE)                                        \
   template <>                                                                  \
-  tq_status launch_reg<LPR>(const RegPlan &pl, bool gate, const RegArgs &a,    \
-                            hipStream_t s) {                                   \
+  tq_status launch_reg_part<LPR, GATE>(const RegPlan &pl, int xt,              \
+                                       const RegArgs &a, hipStream_t s) {      \
     const dim3 grid(pl.blocks), block(kRegThreads);                            \
-    if (gate) {                                                                \
-      TQ_REG_NP_CASES(LPR, true)                                               \
-    }                                                                          \
-    TQ_REG_NP_CASES(LPR, false)                                                \
+    TQ_REG_XT_CASES(LPR, GATE)                                                 \
   }
+
+template <int LPR, bool GATE>
+tq_status launch_reg_part(const RegPlan &pl, int xt, const RegArgs &a,
+                          hipStream_t s);
+
+// Explicit specializations, each defined in its own tq_gemv_reg_l*.hip.
+#define TQ_DECLARE_LAUNCH_REG(LPR, GATE)                                       \
+  template <>                                                                  \
+  tq_status launch_reg_part<LPR, GATE>(const RegPlan &pl, int xt,              \
+                                       const RegArgs &a, hipStream_t s);
+TQ_DECLARE_LAUNCH_REG(16, false)
+TQ_DECLARE_LAUNCH_REG(16, true)
+TQ_DECLARE_LAUNCH_REG(32, false)
+TQ_DECLARE_LAUNCH_REG(32, true)
+TQ_DECLARE_LAUNCH_REG(64, false)
+TQ_DECLARE_LAUNCH_REG(64, true)
+TQ_DECLARE_LAUNCH_REG(128, false)
+TQ_DECLARE_LAUNCH_REG(128, true)
+TQ_DECLARE_LAUNCH_REG(256, false)
+TQ_DECLARE_LAUNCH_REG(256, true)
+#undef TQ_DECLARE_LAUNCH_REG
+
+template <int LPR>
+tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
+                     hipStream_t s) {
+  return gate ? launch_reg_part<LPR, true>(pl, xt, a, s)
+              : launch_reg_part<LPR, false>(pl, xt, a, s);
+}
 
 }  // namespace tq

@@ -1,0 +1,8 @@
+// tq_gemv_reg_l128_gate.hip -- instantiations of the register-resident M = 1
+// GEMV (tq_gemv_reg.h) for 128-lane teams, two weight streams (gate/up); split per
+// team width and stream count so the library builds in parallel.
+#include "tq_gemv_reg.h"
+
+namespace tq {
+TQ_DEFINE_LAUNCH_REG(128, true)
+}  // namespace tq

@@ -149,6 +149,43 @@ TQ_API tq_status tq_gate_up_relu2(const uint8_t *packed_gate, float s_gate,
                            int64_t N, int64_t K, float *h, int32_t *acc_gate,
                            int32_t *acc_up, hipStream_t stream);
 
+/*
+ * tq_quant_gemv -- tq_act_quant followed by tq_gemv at M = 1 in one launch
+ * (the per-token quantization runs in the GEMV prologue; every block
+ * recomputes the row's absmax, then quantizes into LDS).  Results are bit-
+ * identical to the two calls.
+ *   x        [K] bf16 (xt = TQ_BF16) or fp32 (xt = TQ_F32), 16-B aligned.
+ *   packed   uint8 [N/4,K] (16-B aligned), w_scale = s_w.
+ *   y        fp32 [N], output: y[n] = (float)acc[n] * (s_w * s), where s is
+ *            *y_scale when y_scale is non-NULL, else the row's own s_x.
+ *   acc      int32 [N], optional exact sums (NULL = skip).
+ *   xq       int8 [K], output: the quantized row (16-B aligned, required).
+ *   x_scale  fp32 [1], output: s_x (required).
+ *   y_scale  fp32 [1] device pointer or NULL: an activation scale to use in
+ *            the rescale instead of s_x (a caller that treats its input as
+ *            already normalized passes 1/127 here).
+ * With N == 0 only xq and x_scale are produced.  K == 0 or K > 32768 take
+ * two launches internally (same results).
+ */
+TQ_API tq_status tq_quant_gemv(const void *x, tq_dtype xt,
+                               const uint8_t *packed, float w_scale, int64_t N,
+                               int64_t K, float *y, int32_t *acc, int8_t *xq,
+                               float *x_scale, const float *y_scale,
+                               hipStream_t stream);
+
+/*
+ * tq_quant_gate_up_relu2 -- tq_act_quant followed by tq_gate_up_relu2 at
+ * M = 1 in one launch; arguments as tq_quant_gemv and tq_gate_up_relu2.
+ */
+TQ_API tq_status tq_quant_gate_up_relu2(const void *x, tq_dtype xt,
+                                        const uint8_t *packed_gate,
+                                        float s_gate, const uint8_t *packed_up,
+                                        float s_up, int64_t N, int64_t K,
+                                        float *h, int32_t *acc_gate,
+                                        int32_t *acc_up, int8_t *xq,
+                                        float *x_scale, const float *y_scale,
+                                        hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 TQ_API const char *tq_status_string(tq_status status);
 

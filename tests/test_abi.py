@@ -28,10 +28,11 @@ def declared_functions():
     return re.findall(r"TQ_API\s+[\w\s\*]+?\b(tq_\w+)\s*\(", text)
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
     assert set(names) == {"tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
-                          "tq_gate_up_relu2", "tq_status_string"}
+                          "tq_gate_up_relu2", "tq_quant_gemv",
+                          "tq_quant_gate_up_relu2", "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -108,6 +109,27 @@ def test_gemm_small_and_gate_validation(tq):
     assert h(A, 0.02, A, 0.02, A, A, 99, 64, 64, A, None, None, None) == SHAPE
 
 
+def test_quant_gemv_validation(tq):
+    f = tq.lib.tq_quant_gemv
+    #       x  xt  packed   ws   N   K   y  acc  xq  xs  ys  stream
+    assert f(A, 3, A, 0.02, 64, 64, A, None, A, A, None, None) == DTYPE
+    assert f(A, 0, A, 0.02, 62, 64, A, None, A, A, None, None) == SHAPE
+    assert f(A, 0, A, 0.02, 64, 40, A, None, A, A, None, None) == SHAPE
+    assert f(None, 0, A, 0.02, 64, 64, A, None, A, A, None, None) == NULL
+    assert f(A, 0, A, 0.02, 64, 64, A, None, None, A, None, None) == NULL
+    assert f(A, 0, A, 0.02, 64, 64, A, None, A, None, None, None) == NULL
+    assert f(A, 0, None, 0.02, 64, 64, A, None, A, A, None, None) == NULL
+    assert f(A, 0, A, 0.02, 64, 64, None, None, A, A, None, None) == NULL
+    assert f(MIS, 0, A, 0.02, 64, 64, A, None, A, A, None, None) == ALIGN
+    assert f(A, 0, A, 0.02, 64, 64, A, None, MIS, A, None, None) == ALIGN
+    assert f(A, 0, A, 0.02, 64, 64, A, None, A, A, ODD, None) == ALIGN
+    g = tq.lib.tq_quant_gate_up_relu2
+    assert g(A, 1, A, 0.02, None, 0.02, 64, 64, A, None, None, A, A, None,
+             None) == NULL
+    assert g(A, 1, A, 0.02, MIS, 0.02, 64, 64, A, None, None, A, A, None,
+             None) == ALIGN
+
+
 def test_pack_validation(tq):
     f = tq.lib.tq_pack
     assert f(A, 5, 16, A, None) == SHAPE
@@ -132,6 +154,8 @@ def test_no_device_is_reported(tq):
     assert tq.lib.tq_act_quant(A, 0, 1, 64, A, A, None) == DEVICE
     assert tq.lib.tq_pack(A, 8, 16, A, None) == DEVICE
     assert tq.lib.tq_gemm_small(A, 0.02, A, A, 4, 64, 64, A, None, None) == DEVICE
+    assert tq.lib.tq_quant_gemv(A, 0, A, 0.02, 64, 64, A, None, A, A, None,
+                                None) == DEVICE
 
 
 def test_binding_rejects_host_tensors(tq):

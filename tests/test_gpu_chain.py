@@ -30,19 +30,21 @@ def build_layers(torch, tq, oracle, n_layers, cfg=2):
     return dev_layers, ref_layers
 
 
-@pytest.mark.parametrize("n_layers,graph", [(3, False), (30, False), (30, True)])
-def test_chain(n_layers, graph):
+@pytest.mark.parametrize("n_layers,graph,fused", [(3, False, False), (30, False, False),
+                                                   (30, True, False), (30, False, True),
+                                                   (30, True, True)])
+def test_chain(n_layers, graph, fused):
     import torch
     import bit_gemv_tq_amd as tq
     import oracle
     from bit_gemv_tq_amd.chain import DecodeChain
 
-    print(f"chain layers={n_layers} graph={graph}", flush=True)
+    print(f"chain layers={n_layers} graph={graph} fused={fused}", flush=True)
     dev_layers, ref_layers = build_layers(torch, tq, oracle, n_layers)
     h0 = workloads.activations_bf16(1, workloads.HIDDEN, seed=workloads.seed_for(2, 9),
                                     outliers=True)
     h0_dev = torch.from_numpy(h0.view(np.int16)).view(torch.bfloat16).cuda()[0]
-    chain = DecodeChain(dev_layers, "cuda")
+    chain = DecodeChain(dev_layers, "cuda", fused=fused)
     h_ref, st_ref = oracle.decode_chain(ref_layers, h0, keep_stages=True)
 
     if not graph:

@@ -269,3 +269,89 @@ def test_gemm_small_zero_k(env):
     y = tq.tq_gemm_small(packed, 0.5, xq, xs)
     torch.cuda.synchronize()
     assert y.shape == (5, 32) and not y.any()
+
+
+# ------------------------------------------------------------------ fused
+FUSED_SHAPES = [(4, 16), (12, 48), (100, 1008), (36, 2064), (2560, 2560),
+                (6912, 2560), (2560, 6912), (8, 32768), (4, 32784), (28, 16384),
+                (28672, 8192), (8192, 28672)]
+
+
+@pytest.mark.parametrize("N,K", FUSED_SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quant_gemv(env, N, K, dtype):
+    torch, tq, oracle = env
+    say(f"quant_gemv {dtype} N={N} K={K}")
+    codes = workloads.ternary_codes(N, K, seed=N * 5 + K)
+    packed, ref = dev_packed(env, codes)
+    if dtype == "bf16":
+        xh = workloads.activations_bf16(1, K, seed=K + 3, outliers=True)
+        x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).cuda()[0]
+    else:
+        xh = workloads.normal_f32(1, K, seed=K + 4, outliers=True) * np.float32(0.3)
+        x = torch.from_numpy(xh).cuda()[0]
+    s_w = np.float32(0.021)
+    acc = torch.empty(N, dtype=torch.int32, device="cuda")
+    xq = torch.empty(K, dtype=torch.int8, device="cuda")
+    xs = torch.empty(1, dtype=torch.float32, device="cuda")
+    y = tq.tq_quant_gemv(x, packed, s_w, acc=acc, xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.act_quant(xh.reshape(1, K), dtype)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref[0])
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    acc_ref, y32 = oracle.gemv(ref, s_w, q_ref, s_ref, N)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref[0])
+    check_y(y.cpu().numpy(), y32[0], oracle.rescale(acc_ref, s_w, s_ref, exact=True)[0])
+    # with the rescale override (the decode chain's unit activation scale)
+    unit = torch.tensor([np.float32(1) / np.float32(127)], device="cuda")
+    y2 = tq.tq_quant_gemv(x, packed, s_w, xq=xq, x_scale=xs, y_scale=unit)
+    torch.cuda.synchronize()
+    u = unit.cpu().numpy()
+    _, y32u = oracle.gemv(ref, s_w, q_ref, u, N)
+    check_y(y2.cpu().numpy(), y32u[0], oracle.rescale(acc_ref, s_w, u, exact=True)[0])
+
+
+@pytest.mark.parametrize("N,K", [(6912, 2560), (20, 48), (1028, 4608), (256, 28672),
+                                 (8, 40000)])
+def test_quant_gate_up_relu2(env, N, K):
+    torch, tq, oracle = env
+    say(f"quant_gate_up N={N} K={K}")
+    pg, rg = dev_packed(env, workloads.ternary_codes(N, K, seed=11 + N))
+    pu, ru = dev_packed(env, workloads.ternary_codes(N, K, seed=12 + N))
+    xh = workloads.normal_f32(1, K, seed=K + 13, outliers=True)
+    x = torch.from_numpy(xh).cuda()[0]
+    s_g, s_u = workloads.tensor_scale(4), workloads.tensor_scale(5)
+    ag = torch.empty(N, dtype=torch.int32, device="cuda")
+    au = torch.empty(N, dtype=torch.int32, device="cuda")
+    xq = torch.empty(K, dtype=torch.int8, device="cuda")
+    xs = torch.empty(1, dtype=torch.float32, device="cuda")
+    h = tq.tq_quant_gate_up_relu2(x, pg, s_g, pu, s_u, acc_gate=ag, acc_up=au,
+                                  xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.act_quant(xh, "f32")
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref[0])
+    g_ref, u_ref, h32 = oracle.gate_up_relu2(rg, s_g, ru, s_u, q_ref, s_ref, N)
+    np.testing.assert_array_equal(ag.cpu().numpy(), g_ref[0])
+    np.testing.assert_array_equal(au.cpu().numpy(), u_ref[0])
+    np.testing.assert_array_equal(h.cpu().numpy().view(np.uint32), h32[0].view(np.uint32))
+
+
+def test_quant_gemv_edges(env):
+    torch, tq, oracle = env
+    xq = torch.empty(64, dtype=torch.int8, device="cuda")
+    xs = torch.empty(1, dtype=torch.float32, device="cuda")
+    xh = workloads.activations_bf16(1, 64, seed=1)
+    x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).cuda()[0]
+    # N == 0: only the quantized row and its scale are produced
+    tq.tq_quant_gemv(x, torch.empty(0, 64, dtype=torch.uint8, device="cuda"), 0.5,
+                     xq=xq, x_scale=xs)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.act_quant(xh, "bf16")
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref[0])
+    # K == 0: y = 0, s_x = 1e-5/127
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    y = tq.tq_quant_gemv(e, torch.empty(4, 0, dtype=torch.uint8, device="cuda"), 0.5,
+                         xq=torch.empty(0, dtype=torch.int8, device="cuda"), x_scale=xs)
+    torch.cuda.synchronize()
+    assert not y.any()
+    assert xs.cpu().numpy()[0] == np.float32(np.float32(1e-5) / np.float32(127))
