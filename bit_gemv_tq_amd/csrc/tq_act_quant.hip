@@ -5,6 +5,7 @@
 // not describe activation quantization; this is the library's convention
 // (one correctly rounded divide per row, round half to even, symmetric
 // clamp), applied identically wherever an fp32 value decides an int8 code.
+// The clamp never binds (quant4 in tq_device.h gives the bound).
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -25,14 +26,10 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(
   const size_t elem = kBf16 ? 2 : 4;
   const void *xr = reinterpret_cast<const char *>(x) + (size_t)(m * K) * elem;
 
-  float a = 0.0f;
-  for (int64_t p = threadIdx.x; p < kp; p += kAqThreads) {
-    float v[16];
-    load16<kBf16>(xr, p, v);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
-  }
-  a = wave_max(a);
+  uint32_t mb = 0;
+  for (int64_t p = threadIdx.x; p < kp; p += kAqThreads)
+    mb = absmax_bits<kBf16>(load_piece<kBf16>(xr, p), mb);
+  float a = wave_max(absmax_value<kBf16>(mb));
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) wave_max_lds[wave] = a;
   __syncthreads();
@@ -43,17 +40,9 @@ __global__ __launch_bounds__(kAqThreads) void act_quant_kernel(
   const float ap = a > 1e-5f ? a : 1e-5f;
   const float inv = 127.0f / ap;  // correctly rounded fp32 division
 
-  uint4 *qr = reinterpret_cast<uint4 *>(q + m * K);
-  for (int64_t p = threadIdx.x; p < kp; p += kAqThreads) {
-    float v[16];
-    load16<kBf16>(xr, p, v);
-    uint4 o;
-    o.x = quant4(v + 0, inv);
-    o.y = quant4(v + 4, inv);
-    o.z = quant4(v + 8, inv);
-    o.w = quant4(v + 12, inv);
-    qr[p] = o;
-  }
+  u32x4 *qr = reinterpret_cast<u32x4 *>(q + m * K);
+  for (int64_t p = threadIdx.x; p < kp; p += kAqThreads)
+    qr[p] = quant_piece<kBf16>(load_piece<kBf16>(xr, p), inv);
   if (threadIdx.x == 0) s_x[m] = ap / 127.0f;
 }
 
@@ -71,18 +60,17 @@ __global__ __launch_bounds__(kAqRegThreads) void act_quant_reg_kernel(
   const int kp = (int)(K / 16);
   const size_t elem = kBf16 ? 2 : 4;
   const void *xr = reinterpret_cast<const char *>(x) + (size_t)(m * K) * elem;
-  float v[PPT][16];
-  float a = 0.0f;
+  RawPiece<kBf16> v[PPT];
+  uint32_t mb = 0;
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
     const int p = threadIdx.x + i * kAqRegThreads;
     if (p < kp) {
-      load16<kBf16>(xr, p, v[i]);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(v[i][e]));
+      v[i] = load_piece<kBf16>(xr, p);
+      mb = absmax_bits<kBf16>(v[i], mb);
     }
   }
-  a = wave_max(a);
+  float a = wave_max(absmax_value<kBf16>(mb));
   if ((threadIdx.x & (kWave - 1)) == 0) wave_max_lds[threadIdx.x / kWave] = a;
   __syncthreads();
   a = wave_max_lds[0];
@@ -91,18 +79,11 @@ __global__ __launch_bounds__(kAqRegThreads) void act_quant_reg_kernel(
 
   const float ap = a > 1e-5f ? a : 1e-5f;
   const float inv = 127.0f / ap;  // correctly rounded fp32 division
-  uint4 *qr = reinterpret_cast<uint4 *>(q + m * K);
+  u32x4 *qr = reinterpret_cast<u32x4 *>(q + m * K);
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
     const int p = threadIdx.x + i * kAqRegThreads;
-    if (p < kp) {
-      uint4 o;
-      o.x = quant4(v[i] + 0, inv);
-      o.y = quant4(v[i] + 4, inv);
-      o.z = quant4(v[i] + 8, inv);
-      o.w = quant4(v[i] + 12, inv);
-      qr[p] = o;
-    }
+    if (p < kp) qr[p] = quant_piece<kBf16>(v[i], inv);
   }
   if (threadIdx.x == 0) s_x[m] = ap / 127.0f;
 }

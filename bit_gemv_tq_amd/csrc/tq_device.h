@@ -102,46 +102,111 @@ __device__ __forceinline__ int wave_sum(int v) {
 }
 
 // ---------------------------------------------------------------- act quant
-// 16 consecutive activations of one row, widened exactly to fp32.
+// One piece = 16 consecutive activations of a row, kept in its raw input form
+// (bf16: two 16-byte words; fp32: four).
 template <bool kBf16>
-__device__ __forceinline__ void load16(const void *x, int64_t piece,
-                                       float (&v)[16]) {
-  if constexpr (kBf16) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(x) + 2 * piece;
-    const uint4 h[2] = {p[0], p[1]};
+struct RawPiece {
+  static constexpr int kWords = kBf16 ? 2 : 4;
+  u32x4 w[kWords];
+};
+
+template <bool kBf16>
+__device__ __forceinline__ RawPiece<kBf16> load_piece(const void *x,
+                                                      int64_t piece) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(x) + piece * RawPiece<kBf16>::kWords;
+  RawPiece<kBf16> r;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t d[4] = {h[i].x, h[i].y, h[i].z, h[i].w};
+  for (int i = 0; i < RawPiece<kBf16>::kWords; ++i) r.w[i] = p[i];
+  return r;
+}
+
+// Absmax on bit patterns.  For finite floats, |x| orders exactly like the
+// bit pattern with the sign bit cleared, so the row maximum of |x| can be
+// taken with unsigned integer max on raw words: bf16 pairs with one packed
+// 16-bit max per word, fp32 with one 32-bit max.  `m` carries the running
+// maximum (bf16: two halves, folded by absmax_value).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <bool kBf16>
+__device__ __forceinline__ uint32_t absmax_bits(const RawPiece<kBf16> &r,
+                                                uint32_t m) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+  for (int i = 0; i < RawPiece<kBf16>::kWords; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (kBf16) {
+        const u16x2 a = __builtin_bit_cast(u16x2, r.w[i][j] & 0x7fff7fffu);
+        const u16x2 b = __builtin_bit_cast(u16x2, m);
+        m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+      } else {
+        const uint32_t a = r.w[i][j] & 0x7fffffffu;
+        m = a > m ? a : m;
       }
     }
+  return m;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float absmax_value(uint32_t m) {
+  if constexpr (kBf16) {
+    const uint32_t lo = m & 0xffffu, hi = m >> 16;
+    return __uint_as_float((lo > hi ? lo : hi) << 16);
   } else {
-    const float4 *p = reinterpret_cast<const float4 *>(x) + 4 * piece;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 f = p[i];
-      v[4 * i] = f.x;
-      v[4 * i + 1] = f.y;
-      v[4 * i + 2] = f.z;
-      v[4 * i + 3] = f.w;
-    }
+    return __uint_as_float(m);
   }
 }
 
-// Four fp32 values -> four int8 codes clamp(rne(v * inv), -127, 127) in one
-// dword (the per-token quantization of the activations).
-__device__ __forceinline__ uint32_t quant4(const float *v, float inv) {
-  uint32_t out = 0;
+// Four fp32 values -> four int8 codes rne(v * inv) in one dword.
+//
+// Rounding: for |y| < 2^22, fl(y + 1.5*2^23) = 1.5*2^23 + rne(y) exactly
+// (the sum's ulp is 1 and the add rounds half to even), so the low byte of
+// its bit pattern is rne(y) in two's complement.  The product y = fl(v*inv)
+// is rounded on its own first (no contraction into an fma).
+// Clamp: every v of the row has |v| <= a' and inv = fl(127/a'), so
+// |y| <= fl(a' * fl(127/a')) <= 127 + 2^-17 and |rne(y)| <= 127: the clamp
+// to [-127, 127] of the quantization rule never binds and is not applied.
+constexpr float kRneMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ __forceinline__ uint32_t quant4(const float (&v)[4], float inv) {
+#pragma clang fp contract(off)
+  uint32_t b[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float r = __builtin_rintf(v[i] * inv);  // v_rndne_f32: ties to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    out |= ((uint32_t)(int)r & 0xffu) << (8 * i);
+    const float y = v[i] * inv;
+    b[i] = __float_as_uint(y + kRneMagic);
   }
-  return out;
+  // v_perm_b32 byte selects: {src0, src1} = bytes 7..4, 3..0; 0x0c -> 0x00.
+  const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// A whole piece -> 16 int8 codes (16 bytes, in k order).
+template <bool kBf16>
+__device__ __forceinline__ u32x4 quant_piece(const RawPiece<kBf16> &r,
+                                             float inv) {
+  u32x4 q;
+  if constexpr (kBf16) {
+    // word i, dword j holds k = 8i + 2j (low half) and 8i + 2j + 1 (high).
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t w0 = r.w[d / 2][2 * (d % 2)];
+      const uint32_t w1 = r.w[d / 2][2 * (d % 2) + 1];
+      const float v[4] = {__uint_as_float(w0 << 16),
+                          __uint_as_float(w0 & 0xffff0000u),
+                          __uint_as_float(w1 << 16),
+                          __uint_as_float(w1 & 0xffff0000u)};
+      q[d] = quant4(v, inv);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float v[4] = {__uint_as_float(r.w[d][0]), __uint_as_float(r.w[d][1]),
+                          __uint_as_float(r.w[d][2]), __uint_as_float(r.w[d][3])};
+      q[d] = quant4(v, inv);
+    }
+  }
+  return q;
 }
 
 // ---------------------------------------------------------------- epilogue

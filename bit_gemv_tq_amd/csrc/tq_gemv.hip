@@ -203,9 +203,13 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate) {
   pl.lpr = lpr;
   pl.np = (int)((kp + lpr - 1) / lpr);
   pl.exact = (int64_t)pl.np * lpr == kp;
-  const int64_t teams = kRegThreads / lpr;
+  const int bt = reg_block_threads(lpr);
+  const int64_t teams = bt / lpr;
   int64_t blocks = (n4 + teams - 1) / teams;
-  const int64_t cap = (int64_t)num_cus * (gate ? 2 : 3);
+  // Resident blocks per CU (persistent grid): 8-12 waves per CU, measured
+  // best on MI355X; the two-plane gate kernel holds more registers.
+  const int per_cu = bt == 512 ? (gate ? 1 : 2) : (gate ? 2 : 3);
+  const int64_t cap = (int64_t)num_cus * per_cu;
   if (blocks > cap) blocks = cap;
   pl.blocks = (int)(blocks < 1 ? 1 : blocks);
   return pl;

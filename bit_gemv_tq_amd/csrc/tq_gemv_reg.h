@@ -29,6 +29,11 @@
 namespace tq {
 
 constexpr int kRegThreads = 256;
+
+// Block size per team width: 256-lane teams (K > 16384) run two teams per
+// 512-thread block, so the two share one staged (and, for raw rows,
+// quantized) activation row; narrower teams use 256-thread blocks.
+constexpr int reg_block_threads(int lpr) { return lpr >= 256 ? 512 : kRegThreads; }
 constexpr int kRegMaxPieces = 2048;  // K <= 32768 bytes
 
 // Activation forms: kXInt8 = int8 row + scale given (tq_gemv); kXBf16 /
@@ -52,26 +57,6 @@ struct RegArgs {
   const float *y_scale;  // optional [1]: activation scale used in the
                          // rescale instead of s_x (raw forms)
 };
-
-// 16 raw activations of one piece (VPP 16-byte words) widened to fp32.
-template <int XT>
-__device__ __forceinline__ void piece_floats(const u32x4 (&r)[XT == kXBf16 ? 2 : 4],
-                                             float (&f)[16]) {
-  if constexpr (XT == kXBf16) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[8 * i + 2 * j] = __uint_as_float(r[i][j] << 16);
-        f[8 * i + 2 * j + 1] = __uint_as_float(r[i][j] & 0xffff0000u);
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f[4 * i + j] = __uint_as_float(r[i][j]);
-  }
-}
 
 template <int LPR, int NP, bool EXACT, bool kGate, int XT, int BT = kRegThreads>
 __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
@@ -107,7 +92,7 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   };
 
   // 1. Activation loads first (static count).  Thread i stages pieces
-  // i + s*256.  (Native clang vectors: the compiler keeps these in VGPRs.)
+  // i + s*BT.  (Native clang vectors: the compiler keeps these in VGPRs.)
   const u32x4 *xg = reinterpret_cast<const u32x4 *>(
       XT == kXInt8 ? static_cast<const void *>(g.xq) : g.x);
   u32x4 xs[SP][VPP];
@@ -144,19 +129,20 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
     sx = g.x_scale[0];
   } else {
     // Per-token absmax over the whole row (every block, redundantly), then
-    // q = clamp(rne(x * (127/a')), +-127) exactly as tq_act_quant.
-    float a = 0.0f;
+    // q = rne(x * (127/a')) exactly as tq_act_quant.
+    constexpr bool kBf16 = XT == kXBf16;
+    auto raw = [&](int s) {
+      RawPiece<kBf16> r;
 #pragma unroll
-    for (int s = 0; s < SP; ++s) {
-      const int p = (int)threadIdx.x + s * BT;
-      if (p < kp) {
-        float f[16];
-        piece_floats<XT>(xs[s], f);
+      for (int v = 0; v < VPP; ++v) r.w[v] = xs[s][v];
+      return r;
+    };
+    // Slots past the row end hold a re-read of an in-row piece (clamped
+    // index), so they cannot change the maximum.
+    uint32_t mb = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(f[e]));
-      }
-    }
-    a = wave_max(a);
+    for (int s = 0; s < SP; ++s) mb = absmax_bits<kBf16>(raw(s), mb);
+    float a = wave_max(absmax_value<kBf16>(mb));
     if ((threadIdx.x & (kWave - 1)) == 0) amax_lds[wave] = a;
     __syncthreads();
     a = amax_lds[0];
@@ -169,10 +155,7 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
 #pragma unroll
     for (int s = 0; s < SP; ++s) {
       const int p = (int)threadIdx.x + s * BT;
-      float f[16];
-      piece_floats<XT>(xs[s], f);
-      const u32x4 q = {quant4(f + 0, inv), quant4(f + 4, inv),
-                       quant4(f + 8, inv), quant4(f + 12, inv)};
+      const u32x4 q = quant_piece<kBf16>(raw(s), inv);
       x_lds[threadIdx.x + s * BT] = q;
       if (writer && p < kp)
         reinterpret_cast<u32x4 *>(g.xq_out)[p] = q;
@@ -276,8 +259,8 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
                      hipStream_t s);
 
 #define TQ_REG_KERNEL(LPR, NPV, GATE, XT)                                      \
-  (pl.exact ? gemv_reg_kernel<LPR, NPV, true, GATE, XT>                        \
-            : gemv_reg_kernel<LPR, NPV, false, GATE, XT>)
+  (pl.exact ? gemv_reg_kernel<LPR, NPV, true, GATE, XT, reg_block_threads(LPR)> \
+            : gemv_reg_kernel<LPR, NPV, false, GATE, XT, reg_block_threads(LPR)>)
 
 #define TQ_REG_NP_CASES(LPR, GATE, XT)                                         \
   switch (pl.np) {                                                             \
@@ -304,7 +287,7 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
   template <>                                                                  \
   tq_status launch_reg_part<LPR, GATE>(const RegPlan &pl, int xt,              \
                                        const RegArgs &a, hipStream_t s) {      \
-    const dim3 grid(pl.blocks), block(kRegThreads);                            \
+    const dim3 grid(pl.blocks), block(reg_block_threads(LPR));                 \
     TQ_REG_XT_CASES(LPR, GATE)                                                 \
   }
 

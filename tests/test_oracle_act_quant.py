@@ -167,3 +167,39 @@ def test_ieee_helper_known_values():
     assert ieee.rn32(Fraction(1, 1 << 149)) == Fraction(1, 1 << 149)
     assert ieee.rn32(Fraction(1, 1 << 150)) == 0              # tie -> 0 (even)
     assert ieee.rne_int(Fraction(5, 2)) == 2 and ieee.rne_int(Fraction(-5, 2)) == -2
+
+
+def _unclamped_peak(a):
+    """rne(RN32(a * RN32(127 / max(a, 1e-5)))) in numpy float32: the largest
+    unclamped code a row with absmax a can produce (at its absmax element)."""
+    a = np.asarray(a, np.float32)
+    ap = np.maximum(a, np.float32(1e-5))
+    inv = (np.float32(127.0) / ap).astype(np.float32)
+    return np.rint((a * inv).astype(np.float32))
+
+
+def test_clamp_never_binds():
+    # The symmetric clamp of the quantization rule is a no-op for finite
+    # rows: |x| <= a' and inv = RN32(127/a') give RN32(|x| inv) <= 127 + 2^-17,
+    # so |rne(.)| <= 127.  (The GPU kernels rely on this and round without
+    # clamping.)  Exhaustive over every positive finite bf16 absmax, and over
+    # every fp32 significand in [1, 2) (all exponents scale exactly between
+    # 1e-5 and the overflow limit); the product is monotone in |x|, so the
+    # absmax element is the worst case of its row.
+    bits = np.arange(1, 0x7F80, dtype=np.uint32) << 16
+    a_bf16 = bits.view(np.float32)
+    peak = _unclamped_peak(a_bf16)
+    assert peak.max() == 127.0
+    np.testing.assert_array_equal(peak[a_bf16 >= np.float32(1e-5)], 127.0)
+    assert np.all(peak[a_bf16 < np.float32(1e-5)] <= 127.0)
+    sig = (np.uint32(0x3F800000) + np.arange(1 << 23, dtype=np.uint32)).view(np.float32)
+    for e in (-16, 0, 60, 126):
+        a = (sig * np.float32(2.0 ** e)).astype(np.float32)
+        a = a[np.isfinite(a)]
+        np.testing.assert_array_equal(_unclamped_peak(a), 127.0)
+    # The same bound from the exact IEEE model (no numpy float32 arithmetic).
+    rng = np.random.default_rng(11)
+    for a in rng.choice(a_bf16[a_bf16 >= np.float32(1e-5)], 300, replace=False):
+        inv = ieee.rn32(Fraction(127) / Fraction(float(a)))
+        y = ieee.rn32(Fraction(float(a)) * inv)
+        assert y <= 127 + Fraction(1, 1 << 17) and ieee.rne_int(y) == 127
