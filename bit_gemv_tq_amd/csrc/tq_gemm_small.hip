@@ -7,17 +7,29 @@
 // memory bandwidth; post "One GPU, many users": one GPU serving several
 // requests at once, i.e. several activation rows per weight read.
 //
-// Mapping: v_mfma_i32_16x16x64_i8 computes D[16x16] += A[16x64] * B[64x16].
-// A = 16 packed weight rows of one plane, decoded to signed int8 {-1,0,+1}
-// with one v_perm_b32 byte lookup per dword; B = 16 activation rows.  Lane
-// l loads 16 bytes of packed row i0 + (l % 16) at k offset 16*(l / 16) of a
-// 64-byte k step; that one load gives the A operands of all four planes
-// (4 output row blocks).  B is the same 16-byte k block of activation row
-// l % 16.  Because A and B take the same k block per lane, the sum over k
-// does not depend on how the matrix core orders k inside its step.  The
-// eight waves of a block own contiguous k ranges and keep U k steps of loads
-// in flight; their partial tiles are summed in LDS with integer atomics
-// (exact, order free).
+// v_mfma_i32_16x16x64_i8 computes D[16x16] += A[16x64] * B[64x16]; lane l
+// supplies 16 bytes of A row l % 16 and of B column l % 16, both for the
+// same k block (l / 16), so the k order inside a step never matters.  A rows
+// are packed weight rows decoded to signed int8 {-1,0,+1} by one v_perm_b32
+// byte lookup per dword; B columns are activation rows.
+//
+// Two kernel forms, both with one 16-row activation tile per block:
+//  * direct (M <= 16): a tile is TP = 4 or 8 packed rows; MFMA row r is
+//    packed row r / PL, plane r % PL + PL*h (PL = 16/TP planes per MFMA,
+//    4/PL MFMAs per load).  The lanes that share a packed piece load the
+//    same address, so a load touches only TP rows, and small TP gives enough
+//    tiles to spread the weight stream over every CU.
+//  * staged (M > 16): a tile is 16 packed rows (one plane per MFMA, four
+//    MFMAs per load) and M is split over blocks, so each block reads as
+//    many activation rows as weight rows.  Operands are loaded with
+//    contiguous 256-byte row segments (4 rows per load instruction), written
+//    to a wave-private LDS tile with a swizzle that keeps both the writes
+//    (one row, 16 pieces) and the MFMA-layout reads (16 rows, one piece)
+//    free of bank conflicts, then read back as MFMA operands.
+// In both forms the waves of a block own contiguous k ranges; their partial
+// tiles are summed in LDS with integer atomics (exact, order free).  Blocks
+// are mapped to tiles XCD-aware: the M-split blocks of one weight tile run
+// on one XCD, so all but the first read it from that XCD's L2.
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -31,8 +43,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmWaves = 8;
-constexpr int kGemmThreads = kGemmWaves * kWave;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, blocks dispatched round-robin
 
 struct GemmArgs {
   const uint8_t *p0, *p1;
@@ -42,82 +53,100 @@ struct GemmArgs {
   int M, n4, K;
   float *y;
   int32_t *acc0, *acc1;
+  int ntiles, mtiles;  // weight tiles, 16-row activation tiles
 };
 
-// Plane j of a 16-byte piece as signed weights: codes {0,1,2} select the
-// bytes 0xFF, 0x00, 0x01 (-1, 0, +1) of a 4-byte table.
-__device__ __forceinline__ v4i signed_plane(const uint4 &w, int j) {
+// Block -> (weight tile, activation tile).  The grid is padded to a
+// multiple of kXcds * mtiles; block b runs on XCD b % kXcds, and the
+// mtiles consecutive blocks of one XCD share a weight tile.  Returns false
+// for padding blocks (the whole block exits before any barrier).
+__device__ __forceinline__ bool block_tile(const GemmArgs &g, int &tile, int &mt) {
+  const int b = blockIdx.x;
+  const int slot = b / kXcds;
+  tile = (slot / g.mtiles) * kXcds + b % kXcds;
+  mt = slot % g.mtiles;
+  return tile < g.ntiles;
+}
+
+// Signed weights of one plane of a 16-byte piece: codes {0,1,2} select the
+// bytes 0xFF, 0x00, 0x01 (-1, 0, +1) of a 4-byte table.  sh = 2 * plane.
+__device__ __forceinline__ v4i plane_operand(const u32x4 &w, int sh) {
   constexpr uint32_t kTable = 0x000100FFu;
-  const int sh = 2 * j;
   v4i a;
-  a[0] = (int)__builtin_amdgcn_perm(0u, kTable, (w.x >> sh) & 0x03030303u);
-  a[1] = (int)__builtin_amdgcn_perm(0u, kTable, (w.y >> sh) & 0x03030303u);
-  a[2] = (int)__builtin_amdgcn_perm(0u, kTable, (w.z >> sh) & 0x03030303u);
-  a[3] = (int)__builtin_amdgcn_perm(0u, kTable, (w.w >> sh) & 0x03030303u);
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    a[d] = (int)__builtin_amdgcn_perm(0u, kTable, (w[d] >> sh) & 0x03030303u);
   return a;
 }
 
-template <int MT, int U, bool kGate>
-__global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
-  constexpr int NM = kGate ? 2 : 1;
-  constexpr int kTileInts = 64 * 4;               // one 16x16 int32 tile
-  constexpr int kRed = NM * 4 * MT * kTileInts;   // all tiles of the block
-  __shared__ int red[kRed];
+__device__ __forceinline__ v4i as_v4i(const u32x4 &v) {
+  return v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+}
 
-  for (int t = threadIdx.x; t < kRed; t += kGemmThreads) red[t] = 0;
+// Rescale (and gate) one output (m, n) from its exact int32 sums.
+template <bool kGate>
+__device__ __forceinline__ void emit(const GemmArgs &g, int m, size_t n, int v0,
+                                     int v1) {
+  const size_t o = (size_t)m * g.n4 * 4 + n;
+  const float sx = g.x_scale[m];
+  if (g.acc0) g.acc0[o] = v0;
+  if constexpr (kGate) {
+    if (g.acc1) g.acc1[o] = v1;
+    g.y[o] = relu2_gate(rescale(v0, g.s0 * sx), rescale(v1, g.s1 * sx));
+  } else {
+    g.y[o] = rescale(v0, g.s0 * sx);
+  }
+}
+
+// ------------------------------------------------------------ direct form
+template <int TP, int U, int W, bool kGate>
+__global__ __launch_bounds__(W *kWave) void gemm_direct_kernel(GemmArgs g) {
+  constexpr int NM = kGate ? 2 : 1;
+  constexpr int PL = 16 / TP;  // planes per MFMA
+  constexpr int NG = 4 / PL;   // MFMAs per loaded piece
+  __shared__ int red[NM][NG][256];
+  int tile, mt;
+  if (!block_tile(g, tile, mt)) return;
+  for (int t = threadIdx.x; t < NM * NG * 256; t += W * kWave) (&red[0][0][0])[t] = 0;
   __syncthreads();
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int i0 = blockIdx.x * 16;
-  const int prow = min(i0 + (lane & 15), g.n4 - 1);  // past the end: reread
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int r = lane & 15;  // MFMA row (A) / column (B) of this lane
+  const int i0 = tile * TP;
+  const int prow = min(i0 + r / PL, g.n4 - 1);  // past the end: reread
   const int kb = 16 * (lane >> 4);
   const int K = g.K;
   const int nsteps = (K + 63) / 64;
-  const int per = (nsteps + kGemmWaves - 1) / kGemmWaves;
-  const int s0 = min(wave * per, nsteps);
-  const int s1 = min(s0 + per, nsteps);
-
+  const int per = (nsteps + W - 1) / W;
+  const int s0 = min(wave * per, nsteps), s1 = min(s0 + per, nsteps);
   const uint8_t *P[NM];
   P[0] = g.p0 + (size_t)prow * K;
   if constexpr (kGate) P[NM - 1] = g.p1 + (size_t)prow * K;
-  const int8_t *Q[MT];
-  bool qrow_ok[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int row = 16 * t + (lane & 15);
-    qrow_ok[t] = row < g.M;
-    Q[t] = g.xq + (size_t)min(row, g.M - 1) * K;
-  }
+  const bool qok = r < g.M;  // one activation tile: M <= 16
+  const int8_t *Q = g.xq + (size_t)min(r, g.M - 1) * K;
 
-  v4i acc[NM][4][MT];
+  v4i acc[NM][NG];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[m][j][t] = v4i{0, 0, 0, 0};
+    for (int h = 0; h < NG; ++h) acc[m][h] = v4i{0, 0, 0, 0};
 
   for (int s = s0; s < s1; s += U) {
     // U k steps of loads in flight.  Slots past this wave's range (or past
-    // K) read an in-bounds piece and get a zero activation operand.
-    uint4 w[U][NM];
-    v4i b[U][MT];
+    // K: K % 64 may leave a ragged step) reread an in-bounds piece and get a
+    // zero activation operand.
+    u32x4 w[U][NM];
+    v4i b[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kk = (s + u) * 64 + kb;
-      const bool ok = s + u < s1 && kk < K;  // K % 64 may leave a ragged step
+      const bool ok = s + u < s1 && kk < K;
       const int k = ok ? kk : 0;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
-        w[u][m] = load_stream16(reinterpret_cast<const uint4 *>(P[m] + k));
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(Q[t] + k);
-        const bool use = ok && qrow_ok[t];
-        b[u][t] = use ? v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}
-                      : v4i{0, 0, 0, 0};
-      }
+        w[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(P[m] + k));
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(Q + k);
+      b[u] = (ok && qok) ? as_v4i(v) : v4i{0, 0, 0, 0};
     }
     // Keep all U steps of loads ahead of the first MFMA.
     __builtin_amdgcn_sched_barrier(0);
@@ -126,89 +155,186 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(GemmArgs g) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i a = signed_plane(w[u][m], j);
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-            acc[m][j][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[u][t],
-                                                                 acc[m][j][t], 0, 0, 0);
-        }
+        for (int h = 0; h < NG; ++h)
+          acc[m][h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              plane_operand(w[u][m], 2 * (r % PL + PL * h)), b[u], acc[m][h], 0, 0, 0);
   }
 
-  // Exact cross-wave reduction in LDS.
+  // Exact cross-wave reduction, then the epilogue.  D element i of lane l is
+  // row rr = 4*(l/16) + i (packed row i0 + rr/PL, plane rr%PL + PL*h) of
+  // column l % 16 (activation row).
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int h = 0; h < NG; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(&red[m][h][lane * 4 + i], acc[m][h][i]);
+  __syncthreads();
+  for (int h = wave; h < NG; h += W) {
+    if (r >= g.M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * (lane >> 4) + i;
+      const int p = i0 + rr / PL;
+      if (p >= g.n4) continue;
+      const size_t n = (size_t)(rr % PL + PL * h) * g.n4 + p;
+      emit<kGate>(g, r, n, red[0][h][lane * 4 + i], red[NM - 1][h][lane * 4 + i]);
+    }
+  }
+}
+
+// ------------------------------------------------------------ staged form
+constexpr int kStageJ = 16;              // 16-byte pieces per row per batch
+constexpr int kStageSlots = 16 * kStageJ;  // one 16-row operand tile
+
+// LDS slot of piece j (k = batch base + 16 j) of tile row r (0..15).  The
+// bank group of a slot is its index mod 16: (r + j) mod 16 differs across
+// the 16 rows of one piece (MFMA reads) and across 16 pieces of one row
+// (writes), so neither access conflicts.
+__device__ __forceinline__ int stage_slot(int r, int j) {
+  return (j >> 2) * 64 + (j & 3) * 16 + ((r + j) & 15);
+}
+
+template <int W, bool kGate>
+__global__ __launch_bounds__(W *kWave) void gemm_staged_kernel(GemmArgs g) {
+  constexpr int NM = kGate ? 2 : 1;
+  constexpr int RPI = kWave / kStageJ;  // rows per load instruction (4)
+  constexpr int NI = 16 / RPI;          // load instructions per operand tile
+  __shared__ u32x4 stage[W][(NM + 1) * kStageSlots];
+  __shared__ int red[NM][4][256];
+  int tile, mt;
+  if (!block_tile(g, tile, mt)) return;
+  for (int t = threadIdx.x; t < NM * 4 * 256; t += W * kWave) (&red[0][0][0])[t] = 0;
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  u32x4 *As = stage[wave];                      // NM weight tiles
+  u32x4 *Bs = stage[wave] + NM * kStageSlots;   // activation tile
+  const int i0 = tile * 16;
+  const int K = g.K;
+  const int m0 = mt * 16;
+  const int mvalid = min(g.M - m0, 16);
+  // Activation rows >= mvalid stay zero for the whole kernel.
+  for (int t = lane; t < kStageSlots; t += kWave) Bs[t] = u32x4{0, 0, 0, 0};
+  const int nb = (K + 16 * kStageJ - 1) / (16 * kStageJ);
+  const int per = (nb + W - 1) / W;
+  const int b0 = min(wave * per, nb), b1 = min(b0 + per, nb);
+  const int lrow = lane / kStageJ, lj = lane % kStageJ;  // load-side mapping
+  v4i acc[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = v4i{0, 0, 0, 0};
+  __syncthreads();
+
+  for (int bb = b0; bb < b1; ++bb) {
+    const int k = bb * 16 * kStageJ + 16 * lj;
+    const bool kok = k < K;
+    const int kc = kok ? k : K - 16;  // in bounds; its activation is zeroed
+    u32x4 wv[NM][NI], xv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int prow = min(i0 + i * RPI + lrow, g.n4 - 1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint8_t *p = (m == 0 ? g.p0 : g.p1) + (size_t)prow * K + kc;
+        wv[m][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = min(m0 + i * RPI + lrow, g.M - 1);
+      if (i * RPI < mvalid)  // uniform: some row of this load is valid
+        xv[i] = *reinterpret_cast<const u32x4 *>(g.xq + (size_t)row * K + kc);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        As[m * kStageSlots + stage_slot(i * RPI + lrow, lj)] = wv[m][i];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = i * RPI + lrow;
+      if (i * RPI < mvalid)
+        Bs[stage_slot(r, lj)] = (kok && r < mvalid) ? xv[i] : u32x4{0, 0, 0, 0};
+    }
+    // The tile is private to this wave, and a wave's LDS accesses complete
+    // in order; this only keeps the compiler from moving accesses across.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < kStageJ / 4; ++u) {
+      const int slot = stage_slot(lane & 15, 4 * u + (lane >> 4));
+      const v4i b = as_v4i(Bs[slot]);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const u32x4 a = As[m * kStageSlots + slot];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(plane_operand(a, 2 * j), b,
+                                                            acc[m][j], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          atomicAdd(&red[((m * 4 + j) * MT + t) * kTileInts + lane * 4 + i],
-                    acc[m][j][t][i]);
+      for (int i = 0; i < 4; ++i) atomicAdd(&red[m][j][lane * 4 + i], acc[m][j][i]);
   __syncthreads();
-
-  // Epilogue.  Output tile layout of the 16x16 int32 result: lane l holds
-  // rows 4*(l/16) + i (i = 0..3) of column l % 16.  Rows are packed rows
-  // i0 + r of plane j (output n = j*N/4 + i0 + r); columns are activation
-  // rows m = 16 t + c.
-  const size_t N = (size_t)g.n4 * 4;
-  for (int jt = wave; jt < 4 * MT; jt += kGemmWaves) {
-    const int j = jt / MT, t = jt % MT;
-    const int c = lane & 15;
-    const int m = 16 * t + c;
-    if (m >= g.M) continue;
-    const float sx = g.x_scale[m];
-    const float c0 = g.s0 * sx, c1 = g.s1 * sx;
+  // D element i of lane l: packed row i0 + 4*(l/16) + i of plane j, column
+  // (activation row m0 + l % 16).
+  const int mrow = m0 + (lane & 15);
+  for (int j = wave; j < 4; j += W) {
+    if (mrow >= g.M) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 4 * (lane >> 4) + i;
-      if (i0 + r >= g.n4) break;
-      const size_t n = (size_t)j * g.n4 + i0 + r;
-      const size_t o = (size_t)m * N + n;
-      const int v0 = red[((0 * 4 + j) * MT + t) * kTileInts + lane * 4 + i];
-      if (g.acc0) g.acc0[o] = v0;
-      if constexpr (kGate) {
-        const int v1 = red[(((NM - 1) * 4 + j) * MT + t) * kTileInts + lane * 4 + i];
-        if (g.acc1) g.acc1[o] = v1;
-        g.y[o] = relu2_gate(rescale(v0, c0), rescale(v1, c1));
-      } else {
-        g.y[o] = rescale(v0, c0);
-      }
+      const int p = i0 + 4 * (lane >> 4) + i;
+      if (p >= g.n4) continue;
+      emit<kGate>(g, mrow, (size_t)j * g.n4 + p, red[0][j][lane * 4 + i],
+                  red[NM - 1][j][lane * 4 + i]);
     }
   }
 }
 
-// k steps in flight per wave: the whole per-wave range when it is short,
-// fewer for larger M (the activation operands cost 4*MT VGPRs per step).
-template <int MT, bool kGate>
-tq_status launch_gemm_mt(const GemmArgs &a, hipStream_t s) {
-  const dim3 grid((a.n4 + 15) / 16), block(kGemmThreads);
-  const int nsteps = (a.K + 63) / 64;
-  const int per = (nsteps + kGemmWaves - 1) / kGemmWaves;
-  constexpr int kUMax = kGate ? (MT <= 1 ? 8 : (MT == 2 ? 4 : 2))
-                              : (MT <= 2 ? 8 : 4);
-  if constexpr (kUMax == 2) {
-    return launch(gemm_small_kernel<MT, 2, kGate>, grid, block, 0, s, a);
-  } else if constexpr (kUMax == 4) {
-    if (per <= 2) return launch(gemm_small_kernel<MT, 2, kGate>, grid, block, 0, s, a);
-    return launch(gemm_small_kernel<MT, 4, kGate>, grid, block, 0, s, a);
-  } else {
-    if (per <= 2) return launch(gemm_small_kernel<MT, 2, kGate>, grid, block, 0, s, a);
-    if (per <= 4) return launch(gemm_small_kernel<MT, 4, kGate>, grid, block, 0, s, a);
-    return launch(gemm_small_kernel<MT, 8, kGate>, grid, block, 0, s, a);
-  }
+// ------------------------------------------------------------ launch
+// Grid: tiles padded so every XCD gets whole groups of mtiles blocks.
+dim3 gemm_grid(const GemmArgs &a) {
+  const int groups = (a.ntiles + kXcds - 1) / kXcds;
+  return dim3((unsigned)(groups * kXcds * a.mtiles));
 }
 
 template <bool kGate>
-tq_status launch_gemm(int M, const GemmArgs &a, hipStream_t s) {
-  switch ((M + 15) / 16) {
-    case 1: return launch_gemm_mt<1, kGate>(a, s);
-    case 2: return launch_gemm_mt<2, kGate>(a, s);
-    case 3: return launch_gemm_mt<3, kGate>(a, s);
-    case 4: return launch_gemm_mt<4, kGate>(a, s);
+tq_status launch_gemm(GemmArgs a, int num_cus, hipStream_t s) {
+  if (a.M <= 16) {
+    // Direct form.  Tile height: 8 packed rows while that still gives about
+    // one tile per CU (measured: taller tiles cut activation re-reads),
+    // else 4 so the weight stream is spread over every CU.
+    a.mtiles = 1;
+    if ((int64_t)a.n4 >= 8LL * num_cus * 3 / 4) {
+      a.ntiles = (a.n4 + 7) / 8;
+      return launch(gemm_direct_kernel<8, 4, 16, kGate>, gemm_grid(a),
+                    dim3(16 * kWave), 0, s, a);
+    }
+    a.ntiles = (a.n4 + 3) / 4;
+    if constexpr (kGate)
+      return launch(gemm_direct_kernel<4, 4, 8, kGate>, gemm_grid(a),
+                    dim3(8 * kWave), 0, s, a);
+    else
+      return launch(gemm_direct_kernel<4, 8, 8, kGate>, gemm_grid(a),
+                    dim3(8 * kWave), 0, s, a);
   }
-  return TQ_ERR_SHAPE;
+  // Staged form, M split into 16-row blocks.  About two 256-byte k batches
+  // per wave (16 waves for long rows); the gated form holds two weight
+  // tiles per wave, so it stays at 8 waves (LDS).
+  a.mtiles = (a.M + 15) / 16;
+  a.ntiles = (a.n4 + 15) / 16;
+  const int nb = (a.K + 255) / 256;
+  if (!kGate && nb >= 20)
+    return launch(gemm_staged_kernel<16, false>, gemm_grid(a), dim3(16 * kWave), 0,
+                  s, a);
+  return launch(gemm_staged_kernel<8, kGate>, gemm_grid(a), dim3(8 * kWave), 0, s, a);
 }
 
 tq_status gemm_small(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
@@ -232,8 +358,9 @@ tq_status gemm_small(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
   a.y = y;
   a.acc0 = acc0;
   a.acc1 = acc1;
-  return p1 ? launch_gemm<true>((int)M, a, stream)
-            : launch_gemm<false>((int)M, a, stream);
+  a.ntiles = a.mtiles = 0;  // set by the launcher
+  return p1 ? launch_gemm<true>(a, dev.num_cus, stream)
+            : launch_gemm<false>(a, dev.num_cus, stream);
 }
 
 tq_status check_common(const uint8_t *p, const int8_t *xq, const float *x_scale,

@@ -206,7 +206,8 @@ def test_gemv_zero_k_and_empty(env):
 # ------------------------------------------------------------------ gate/up
 @pytest.mark.parametrize("M,N,K", [(1, 6912, 2560), (1, 20, 48), (1, 100, 1008),
                                    (1, 256, 28672), (1, 8, 40000), (1, 1028, 4608),
-                                   (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560)])
+                                   (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560),
+                                   (16, 2052, 112), (33, 260, 400), (64, 2560, 6912)])
 def test_gate_up_relu2(env, M, N, K):
     torch, tq, oracle = env
     say(f"gate_up M={M} N={N} K={K}")
