@@ -4,7 +4,8 @@ Step (the `value` line): one pass of the hot path over the shapes the metric
 names, [N, K] = [2560, 6912] (2B-4T down projection) and [8192, 28672]
 (70B-class down projection), plus the transposed 70B-class shape
 [28672, 8192]: for each, per-token int8 quantization of a bf16 activation
-(tq_act_quant) then the ternary GEMV with its fp32 rescale (tq_gemv).
+and the ternary GEMV with its fp32 rescale, in one launch (tq_quant_gemv;
+bit-identical to tq_act_quant followed by tq_gemv, which is timed too).
 `value` = packed weight bytes per step / step time (GB/s).
 
 Inputs: seeded synthetic ternary weights (P(0) = 0.35), packed on the GPU
@@ -17,10 +18,10 @@ Timing:
   * Steps and kernel loops are captured in HIP graphs; a spin kernel queued
     before the start event keeps the host ahead, so HIP events on the
     launch stream measure GPU execution only.
-  * roofline: the dominant kernel (the [8192, 28672] GEMV) is timed as a
-    graph of back-to-back launches over its pool; algorithmic bytes per
-    launch (packed weights + int8 x + fp32 scale + fp32 y) / time per
-    launch, against 8 TB/s.  Back-to-back time includes the short gap
+  * roofline: the dominant kernel (the fused [8192, 28672] launch) is timed
+    as a graph of back-to-back launches over its pool; algorithmic bytes per
+    launch (packed weights + bf16 x + int8 x written + fp32 scale + fp32 y)
+    / time per launch, against 8 TB/s.  Back-to-back time includes the short gap
     between graph nodes, so it is an upper bound on the kernel duration
     that rocprofv3's kernel trace reports.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
@@ -54,7 +55,7 @@ INT8_MFMA_PEAK_TOPS = 5000.0
 POOL_BYTES_MIN = 640 << 20
 STEP_COPIES = 12
 SPIN = 20_000_000
-COUNTER_FILE = os.path.join(ROOT, "profiles", "tq_gemv_8192x28672_counters.txt")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "tq_quant_gemv_8192x28672_counters.txt")
 KERNEL_SOURCES = ("bit_gemv_tq_amd/csrc/tq_gemv_reg.h",
                   "bit_gemv_tq_amd/csrc/tq_gemv.hip",
                   "bit_gemv_tq_amd/csrc/tq_device.h")
@@ -71,6 +72,11 @@ def weight_bytes(N, K):
 def algo_bytes(N, K, M=1):
     # packed weights + int8 activations + fp32 x_scale + fp32 outputs
     return N * K // 4 + M * K + 4 * M + 4 * M * N
+
+
+def algo_bytes_fused(N, K):
+    # packed weights + bf16 row read + int8 row and scale written + fp32 y
+    return N * K // 4 + 2 * K + K + 4 + 4 * N
 
 
 def kernel_source_hash():
@@ -226,6 +232,11 @@ def main():
 
     def step(i):
         for name in SHAPES:
+            tq.tq_quant_gemv(x[name], pools[name][i % STEP_COPIES], s_w, y[name],
+                             xq=xq[name], x_scale=xs[name])
+
+    def step_unfused(i):
+        for name in SHAPES:
             tq.tq_act_quant(x[name], xq[name], xs[name])
             tq.tq_gemv(pools[name][i % STEP_COPIES], s_w, xq[name], xs[name], y[name])
 
@@ -241,33 +252,45 @@ def main():
     step_wbytes = sum(weight_bytes(*s) for s in SHAPES.values())
     value = step_wbytes / (ms_step * 1e-3) / 1e9
     log(f"step: {ms_step * 1e3:.2f} us -> {value:.0f} GB/s")
+    graphs_u = [timer.graph(lambda i=i: step_unfused(i)) for i in range(STEP_COPIES)]
+    ms_step_u = timer.time_graphs(graphs_u, args.steps)
+    log(f"unfused step (act_quant + gemv launches): {ms_step_u * 1e3:.2f} us")
+    del graphs_u
 
     # ------------------------------------------------- per-kernel loops
     R = args.kernel_reps
 
-    def gemv_loop(name, start):
+    def gemv_loop(name, start, fused):
         P = pools[name]
         for r in range(R):
-            tq.tq_gemv(P[(start + r) % len(P)], s_w, xq[name], xs[name], y[name])
+            if fused:
+                tq.tq_quant_gemv(x[name], P[(start + r) % len(P)], s_w, y[name],
+                                 xq=xq[name], x_scale=xs[name])
+            else:
+                tq.tq_gemv(P[(start + r) % len(P)], s_w, xq[name], xs[name], y[name])
 
     per_shape = {}
     for name, (N, K) in SHAPES.items():
         tq.tq_act_quant(x[name], xq[name], xs[name])
         nP = len(pools[name])
-        gs = [timer.graph(lambda name=name, s=s: gemv_loop(name, s))
-              for s in range(0, nP, max(1, nP // 4))][:4]
-        us = timer.time_graphs(gs, 8) * 1e3 / R
-        per_shape[name] = {
-            "N": N, "K": K, "us_per_launch": round(us, 3),
-            "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1),
-            "pct_hbm_peak": round(100 * weight_bytes(N, K) / us / 1e3 / HBM_PEAK_GBS, 1),
-            "algo_GBs": round(algo_bytes(N, K) / us / 1e3, 1),
-        }
-        log(f"gemv {name}: {per_shape[name]}")
+        row = {"N": N, "K": K}
+        for fused in (True, False):
+            gs = [timer.graph(lambda name=name, s=s, f=fused: gemv_loop(name, s, f))
+                  for s in range(0, nP, max(1, nP // 4))][:4]
+            us = timer.time_graphs(gs, 8) * 1e3 / R
+            ab = algo_bytes_fused(N, K) if fused else algo_bytes(N, K)
+            row["quant_gemv" if fused else "gemv"] = {
+                "us_per_launch": round(us, 3),
+                "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1),
+                "pct_hbm_peak": round(100 * weight_bytes(N, K) / us / 1e3 / HBM_PEAK_GBS, 1),
+                "algo_GBs": round(ab / us / 1e3, 1)}
+            del gs
+        per_shape[name] = row
+        log(f"{name}: {row}")
 
     dN, dK = SHAPES[DOMINANT]
-    dom_us = per_shape[DOMINANT]["us_per_launch"]
-    achieved = algo_bytes(dN, dK) / dom_us / 1e3
+    dom_us = per_shape[DOMINANT]["quant_gemv"]["us_per_launch"]
+    achieved = algo_bytes_fused(dN, dK) / dom_us / 1e3
 
     rows = {}
     if not args.no_rows:
@@ -296,17 +319,18 @@ def main():
             "pool_copies_per_shape": {k: len(v) for k, v in pools.items()},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "unfused_ms_per_step": round(ms_step_u, 5),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"gemv_reg_kernel, tq_gemv [N,K]=[{dN},{dK}]",
+            "kernel": f"gemv_reg_kernel (bf16 prologue), tq_quant_gemv [N,K]=[{dN},{dK}]",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": read_traffic(),
             "us_per_launch": dom_us,
-            "bytes_per_launch": algo_bytes(dN, dK),
+            "bytes_per_launch": algo_bytes_fused(dN, dK),
         },
         "per_shape": per_shape,
         "rows": rows,
@@ -333,12 +357,13 @@ def counters_run(torch, tq, workloads, dev):
         P.append(tq.tq_pack(w))
         del w
     xb = workloads.activations_bf16(1, K, seed=4243)
-    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
-    q, s = tq.tq_act_quant(xt)
+    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)[0]
+    q = torch.empty(K, dtype=torch.int8, device=dev)
+    s = torch.empty(1, dtype=torch.float32, device=dev)
     yy = torch.empty(N, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     for r in range(8):
-        tq.tq_gemv(P[r % 4], 0.02, q, s, yy)
+        tq.tq_quant_gemv(xt, P[r % 4], 0.02, yy, xq=q, x_scale=s)
     torch.cuda.synchronize()
     log("counters run done")
 
@@ -451,19 +476,22 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
             scale[name] = workloads.tensor_scale(t)
             del w
         layers.append(Layer(packed, scale))
-    chain = DecodeChain(layers, dev)
     h0b = workloads.activations_bf16(1, workloads.HIDDEN, seed=97, outliers=True)
     h0 = torch.from_numpy(h0b.view(np.int16)).view(torch.bfloat16).to(dev)[0]
-    g = timer.graph(lambda: chain.step(h0))
-    ms = timer.time_graphs([g], 20)
     layer_bytes = sum(weight_bytes(*s) for s in workloads.LAYER_2B4T.values())
     total = layer_bytes * workloads.CHAIN_LAYERS
-    rows["decode_chain_30x2b4t"] = {
-        "us_per_token": round(ms * 1e3, 2),
-        "tokens_per_s": round(1e3 / ms, 1),
-        "weight_GBs": round(total / (ms * 1e-3) / 1e9, 1),
-        "launches_per_token": 10 * workloads.CHAIN_LAYERS}
-    log(f"chain: {rows['decode_chain_30x2b4t']}")
+    for fused, key, launches in ((True, "decode_chain_30x2b4t", 4),
+                                 (False, "decode_chain_30x2b4t_unfused", 10)):
+        chain = DecodeChain(layers, dev, fused=fused)
+        g = timer.graph(lambda: chain.step(h0))
+        ms = timer.time_graphs([g], 20)
+        rows[key] = {
+            "us_per_token": round(ms * 1e3, 2),
+            "tokens_per_s": round(1e3 / ms, 1),
+            "weight_GBs": round(total / (ms * 1e-3) / 1e9, 1),
+            "launches_per_token": launches * workloads.CHAIN_LAYERS}
+        log(f"{key}: {rows[key]}")
+        del g, chain
     return rows
 
 

@@ -29,7 +29,7 @@ STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN",
 
 EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
            "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
-           "tq_status_string")
+           "tq_quant_gemv_group", "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
         "tq_quant_gemv": [p, i32, p, f32, i64, i64, p, p, p, p, p, p],
         "tq_quant_gate_up_relu2": [p, i32, p, f32, p, f32, i64, i64, p, p, p,
                                    p, p, p, p],
+        # host arrays: packed**, w_scale*, N*, y**, acc** (ctypes arrays)
+        "tq_quant_gemv_group": [p, i32, i32, p, p, p, i64, p, p, p, p, p, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -252,6 +254,50 @@ def tq_quant_gemv(x, packed, w_scale, y=None, acc=None, xq=None, x_scale=None,
         _need(y_scale, "y_scale", torch.float32, dev)
     _check("tq_quant_gemv", lib.tq_quant_gemv(
         _ptr(x), xt, _ptr(packed), float(w_scale), N, K, _ptr(y), _ptr(acc),
+        _ptr(xq), _ptr(x_scale), _ptr(y_scale), _stream(stream)))
+    return y
+
+
+def tq_quant_gemv_group(x, packed, w_scale, y=None, acc=None, xq=None,
+                        x_scale=None, y_scale=None, stream=None):
+    """tq_quant_gemv over several matrices sharing x, in one launch.
+    packed / w_scale: lists (1..4 entries); y / acc: optional lists of
+    outputs (entries may be None in acc).  Returns the list of y."""
+    torch = _torch()
+    xt = _raw_row(x)
+    count = len(packed)
+    if not 1 <= count <= 4 or len(w_scale) != count:
+        raise ValueError("need 1..4 matrices and one scale each")
+    dev = packed[0].device
+    K = packed[0].shape[1]
+    for P in packed:
+        _need(P, "packed", torch.uint8, x.device)
+        if P.shape[1] != K:
+            raise ValueError("all matrices must share K")
+    if x.numel() != K:
+        raise ValueError(f"x has {x.numel()} elements, need K={K}")
+    Ns = [P.shape[0] * 4 for P in packed]
+    y = [None] * count if y is None else list(y)
+    y = [_out(t, "y", (n,), torch.float32, dev) for t, n in zip(y, Ns)]
+    if acc is not None:
+        acc = [None if t is None else _out(t, "acc", (n,), torch.int32, dev)
+               for t, n in zip(acc, Ns)]
+    xq = _out(xq, "xq", (K,), torch.int8, dev)
+    x_scale = _out(x_scale, "x_scale", (1,), torch.float32, dev)
+    if y_scale is not None:
+        _need(y_scale, "y_scale", torch.float32, dev)
+    VP = ctypes.c_void_p * count
+    addr = lambda t: None if t is None else t.data_ptr()
+    c_packed = VP(*[addr(P) for P in packed])
+    c_scale = (ctypes.c_float * count)(*[float(s) for s in w_scale])
+    c_n = (ctypes.c_int64 * count)(*Ns)
+    c_y = VP(*[addr(t) for t in y])
+    c_acc = None if acc is None else VP(*[addr(t) for t in acc])
+    _check("tq_quant_gemv_group", lib.tq_quant_gemv_group(
+        _ptr(x), xt, count, ctypes.cast(c_packed, ctypes.c_void_p),
+        ctypes.cast(c_scale, ctypes.c_void_p), ctypes.cast(c_n, ctypes.c_void_p),
+        K, ctypes.cast(c_y, ctypes.c_void_p),
+        None if c_acc is None else ctypes.cast(c_acc, ctypes.c_void_p),
         _ptr(xq), _ptr(x_scale), _ptr(y_scale), _stream(stream)))
     return y
 

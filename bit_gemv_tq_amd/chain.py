@@ -23,7 +23,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import (tq_act_quant, tq_gate_up_relu2, tq_gemv, tq_quant_gate_up_relu2,
-               tq_quant_gemv)
+               tq_quant_gemv, tq_quant_gemv_group)
 
 PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -45,8 +45,9 @@ class DecodeChain:
     """Preallocated buffers and the launch sequence of one decode step.
 
     fused=False: ten launches per layer (separate act-quant launches);
-    fused=True: six, each projection quantizing its own input in the GEMV
-    prologue (tq_quant_gemv / tq_quant_gate_up_relu2).  Both give
+    fused=True: four, each launch quantizing its own input in the GEMV
+    prologue (q, k and v in one grouped launch, tq_quant_gemv_group; then
+    tq_quant_gemv for o and down, tq_quant_gate_up_relu2).  Both give
     bit-identical stages."""
 
     def __init__(self, layers, device, fused=False):
@@ -93,9 +94,10 @@ class DecodeChain:
 
     def layer_fused(self, L: Layer, h_in, h_out, record=None, stream=None):
         u, st = self.unit, stream
-        for name, out in (("q", self.q), ("k", self.k), ("v", self.v)):
-            tq_quant_gemv(h_in, L.packed[name], L.scale[name], out,
-                          xq=self.q8_in, x_scale=self.s_in, y_scale=u, stream=st)
+        tq_quant_gemv_group(h_in, [L.packed[n] for n in ("q", "k", "v")],
+                            [L.scale[n] for n in ("q", "k", "v")],
+                            [self.q, self.k, self.v], xq=self.q8_in,
+                            x_scale=self.s_in, y_scale=u, stream=st)
         tq_quant_gemv(self.q, L.packed["o"], L.scale["o"], self.o,
                       xq=self.q8_o, x_scale=self.s_o, y_scale=u, stream=st)
         tq_quant_gate_up_relu2(self.o, L.packed["gate"], L.scale["gate"],

@@ -300,7 +300,78 @@ tq_status check_quant_args(const void *x, tq_dtype xt, const uint8_t *p,
   return TQ_OK;
 }
 
+// Grouped form: `count` matrices sharing one raw activation row, one launch
+// over their concatenated packed rows (the fallback for K == 0 or
+// K > 32768 quantizes once and runs one GEMV per matrix).
+tq_status quant_gemv_group(const void *x, tq_dtype xt, int count,
+                           const uint8_t *const *packed, const float *w_scale,
+                           const int64_t *N, int64_t K, float *const *y,
+                           int32_t *const *acc, int8_t *xq, float *x_scale,
+                           const float *y_scale, hipStream_t stream) {
+  DeviceInfo dev;
+  if (tq_status s = current_device(&dev)) return s;
+  const int64_t kp = K / 16;
+  RegArgs a{};
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    if (N[i] == 0) continue;  // empty matrices take no rows
+    const int q = a.seg.n++;
+    total += N[i] / 4;
+    a.seg.end[q] = (int)total;
+    a.seg.p[q] = packed[i];
+    a.seg.s[q] = w_scale[i];
+    a.seg.y[q] = y[i];
+    a.seg.acc[q] = acc ? acc[i] : nullptr;
+  }
+  if (total > 0 && kp >= 1 && kp <= kRegMaxPieces) {
+    a.n4 = (int)total;
+    a.kp = (int)kp;
+    a.x = x;
+    a.xq_out = xq;
+    a.xs_out = x_scale;
+    a.y_scale = y_scale;
+    a.p0 = a.seg.p[0];  // unused by the grouped form; kept valid
+    a.y = a.seg.y[0];
+    return launch_gemv_reg(plan_gemv_reg(total, kp, dev.num_cus, false), false,
+                           xt == TQ_BF16 ? kXBf16 : kXF32, a, stream);
+  }
+  if (tq_status s = tq_act_quant(x, xt, 1, K, xq, x_scale, stream)) return s;
+  for (int i = 0; i < count; ++i) {
+    if (N[i] == 0) continue;
+    if (tq_status s = gemv_m1(packed[i], w_scale[i], nullptr, 0.0f, xq,
+                              y_scale ? y_scale : x_scale, N[i], K, y[i],
+                              acc ? acc[i] : nullptr, nullptr, stream))
+      return s;
+  }
+  return TQ_OK;
+}
+
 }  // namespace tq
+
+extern "C" tq_status tq_quant_gemv_group(const void *x, tq_dtype xt,
+                                         int32_t count,
+                                         const uint8_t *const *packed,
+                                         const float *w_scale, const int64_t *N,
+                                         int64_t K, float *const *y,
+                                         int32_t *const *acc, int8_t *xq,
+                                         float *x_scale, const float *y_scale,
+                                         hipStream_t stream) {
+  using namespace tq;
+  if (xt != TQ_BF16 && xt != TQ_F32) return TQ_ERR_DTYPE;
+  if (count < 1 || count > kMaxSeg) return TQ_ERR_SHAPE;
+  if (!packed || !w_scale || !N || !y) return TQ_ERR_NULL;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    if (tq_status s = check_quant_args(x, xt, packed[i], N[i], K, y[i],
+                                       acc ? acc[i] : nullptr, nullptr, xq,
+                                       x_scale, y_scale))
+      return s;
+    total += N[i];
+  }
+  if (total / 4 > (int64_t)INT32_MAX) return TQ_ERR_SHAPE;
+  return quant_gemv_group(x, xt, count, packed, w_scale, N, K, y, acc, xq,
+                          x_scale, y_scale, stream);
+}
 
 extern "C" tq_status tq_quant_gemv(const void *x, tq_dtype xt,
                                    const uint8_t *packed, float w_scale,

@@ -40,6 +40,19 @@ constexpr int kRegMaxPieces = 2048;  // K <= 32768 bytes
 // kXF32 = raw row, quantized in the prologue (tq_quant_gemv).
 constexpr int kXInt8 = 0, kXBf16 = 1, kXF32 = 2;
 
+// Grouped form: several weight matrices with the same K that read one
+// activation row (e.g. the q, k and v projections), run as one packed-row
+// range.  Segment q holds global packed rows [end[q-1], end[q]).
+constexpr int kMaxSeg = 4;
+struct RegSegs {
+  int n;                         // 0: single matrix (p0, s0, y, acc0)
+  int end[kMaxSeg];              // cumulative packed-row counts
+  const uint8_t *p[kMaxSeg];     // packed [N_q/4, K]
+  float s[kMaxSeg];              // weight scales
+  float *y[kMaxSeg];             // [N_q] outputs
+  int32_t *acc[kMaxSeg];         // optional [N_q]
+};
+
 struct RegArgs {
   const uint8_t *p0;     // packed [N/4,K] (gate when kGate)
   const uint8_t *p1;     // packed up (kGate only)
@@ -56,7 +69,29 @@ struct RegArgs {
   float *xs_out;         // [1] its scale s_x, written by block 0 (raw forms)
   const float *y_scale;  // optional [1]: activation scale used in the
                          // rescale instead of s_x (raw forms)
+  RegSegs seg;           // grouped form (not with kGate); n4 = total rows
 };
+
+// Segment of global packed row i (grouped form): its first row and index.
+__device__ __forceinline__ int seg_of(const RegSegs &sg, int i, int &start) {
+  int q = 0;
+  start = 0;
+#pragma unroll
+  for (int t = 1; t < kMaxSeg; ++t)
+    if (t < sg.n && i >= sg.end[t - 1]) {
+      q = t;
+      start = sg.end[t - 1];
+    }
+  return q;
+}
+
+template <typename T>
+__device__ __forceinline__ T seg_pick(const T (&v)[kMaxSeg], int q) {
+  T r = v[0];  // unrolled selects: q may differ between lanes
+#pragma unroll
+  for (int t = 1; t < kMaxSeg; ++t) r = q == t ? v[t] : r;
+  return r;
+}
 
 template <int LPR, int NP, bool EXACT, bool kGate, int XT, int BT = kRegThreads>
 __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
@@ -112,6 +147,12 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const uint4 *rp = P[m] + (size_t)row * kp;
+      if (!kGate && g.seg.n > 0) {  // grouped: the row's own matrix
+        int start;
+        const int q = seg_of(g.seg, row, start);
+        rp = reinterpret_cast<const uint4 *>(seg_pick(g.seg.p, q)) +
+             (size_t)(row - start) * kp;
+      }
 #pragma unroll
       for (int t = 0; t < NP; ++t) w[m][t] = load_stream16(rp + piece(t));
     }
@@ -198,15 +239,25 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
     const int i = rbase + team;
     auto emit = [&](int j, int v0, int v1) {
       if (i >= n4) return;
-      const size_t n = (size_t)j * n4 + i;
       const int sh = j == 0 ? 0 : (j == 1 ? 2 : 4);
       const int t0 = v0 >> sh;  // exact: the sum is a multiple of 1 << sh
-      if (g.acc0) g.acc0[n] = t0;
       if constexpr (kGate) {
+        const size_t n = (size_t)j * n4 + i;
         const int t1 = v1 >> sh;
+        if (g.acc0) g.acc0[n] = t0;
         if (g.acc1) g.acc1[n] = t1;
         g.y[n] = relu2_gate(rescale(t0, c0), rescale(t1, c1));
+      } else if (g.seg.n > 0) {
+        int start;
+        const int q = seg_of(g.seg, i, start);
+        const int n4q = seg_pick(g.seg.end, q) - start;
+        const size_t n = (size_t)j * n4q + (i - start);
+        int32_t *acc = seg_pick(g.seg.acc, q);
+        if (acc) acc[n] = t0;
+        seg_pick(g.seg.y, q)[n] = rescale(t0, seg_pick(g.seg.s, q) * sx);
       } else {
+        const size_t n = (size_t)j * n4 + i;
+        if (g.acc0) g.acc0[n] = t0;
         g.y[n] = rescale(t0, c0);
       }
     };

@@ -186,6 +186,32 @@ TQ_API tq_status tq_quant_gate_up_relu2(const void *x, tq_dtype xt,
                                         float *x_scale, const float *y_scale,
                                         hipStream_t stream);
 
+/*
+ * tq_quant_gemv_group -- `count` ternary GEMVs that read the same raw
+ * activation row, in one launch: tq_quant_gemv for each matrix, with one
+ * shared quantization (the q, k and v projections of an attention layer,
+ * whose inputs are the same normalized hidden state; [ISSUE] "Weight
+ * mapping": q_proj [2560,2560], k_proj and v_proj [640,2560]).
+ *   count    1..4.
+ *   packed, w_scale, N, y, acc: HOST arrays of `count` entries (the one
+ *            exception to the device-memory rule): matrix i is packed[i]
+ *            (uint8 [N[i]/4,K], device, 16-B aligned) with scale w_scale[i],
+ *            writing y[i] (fp32 [N[i]], device) and, when acc is non-NULL
+ *            and acc[i] non-NULL, acc[i] (int32 [N[i]], device).
+ *   x, xt, K, xq, x_scale, y_scale: as tq_quant_gemv (all matrices share K
+ *            and the activation scale).
+ * Every y[i] is bit-identical to tq_quant_gemv on matrix i alone.  Matrices
+ * with N[i] == 0 are skipped.  The host arrays are read before the call
+ * returns and may be reused at once.
+ */
+TQ_API tq_status tq_quant_gemv_group(const void *x, tq_dtype xt, int32_t count,
+                                     const uint8_t *const *packed,
+                                     const float *w_scale, const int64_t *N,
+                                     int64_t K, float *const *y,
+                                     int32_t *const *acc, int8_t *xq,
+                                     float *x_scale, const float *y_scale,
+                                     hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 TQ_API const char *tq_status_string(tq_status status);
 

@@ -32,7 +32,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     assert set(names) == {"tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
                           "tq_gate_up_relu2", "tq_quant_gemv",
-                          "tq_quant_gate_up_relu2", "tq_status_string"}
+                          "tq_quant_gate_up_relu2", "tq_quant_gemv_group",
+                          "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -130,6 +131,33 @@ def test_quant_gemv_validation(tq):
              None) == ALIGN
 
 
+def test_quant_gemv_group_validation(tq):
+    f = tq.lib.tq_quant_gemv_group
+    VP = ctypes.c_void_p * 3
+    packed = VP(0x10000, 0x20000, 0x30000)
+    scale = (ctypes.c_float * 3)(0.02, 0.03, 0.04)
+    ys = VP(0x40000, 0x50000, 0x60000)
+
+    def call(count=3, xt=1, Ns=(64, 16, 16), K=64, packed=packed, ys=ys,
+             acc=None, x=A, xq=A, xs=A, ysc=None):
+        n = (ctypes.c_int64 * 3)(*Ns)
+        c = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+        return f(x, xt, count, c(packed), c(scale), c(n), K, c(ys), c(acc),
+                 xq, xs, ysc, None)
+    assert call(count=0) == SHAPE
+    assert call(count=5) == SHAPE
+    assert call(xt=2) == DTYPE
+    assert call(Ns=(64, 18, 16)) == SHAPE
+    assert call(K=40) == SHAPE
+    assert call(packed=None) == NULL
+    assert call(ys=None) == NULL
+    assert call(ys=VP(0x40000, None, 0x60000)) == NULL
+    assert call(packed=VP(0x10000, 0x20004, 0x30000)) == ALIGN
+    assert call(acc=VP(None, 0x70001, None)) == ALIGN
+    assert call(x=MIS) == ALIGN
+    assert call(xq=None) == NULL
+
+
 def test_pack_validation(tq):
     f = tq.lib.tq_pack
     assert f(A, 5, 16, A, None) == SHAPE
@@ -156,6 +184,12 @@ def test_no_device_is_reported(tq):
     assert tq.lib.tq_gemm_small(A, 0.02, A, A, 4, 64, 64, A, None, None) == DEVICE
     assert tq.lib.tq_quant_gemv(A, 0, A, 0.02, 64, 64, A, None, A, A, None,
                                 None) == DEVICE
+    one = (ctypes.c_void_p * 1)(0x10000)
+    assert tq.lib.tq_quant_gemv_group(
+        A, 0, 1, ctypes.cast(one, ctypes.c_void_p),
+        ctypes.cast((ctypes.c_float * 1)(0.02), ctypes.c_void_p),
+        ctypes.cast((ctypes.c_int64 * 1)(64), ctypes.c_void_p), 64,
+        ctypes.cast(one, ctypes.c_void_p), None, A, A, None, None) == DEVICE
 
 
 def test_binding_rejects_host_tensors(tq):

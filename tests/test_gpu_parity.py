@@ -312,6 +312,62 @@ def test_quant_gemv(env, N, K, dtype):
     check_y(y2.cpu().numpy(), y32u[0], oracle.rescale(acc_ref, s_w, u, exact=True)[0])
 
 
+GROUP_CASES = [((2560, 640, 640), 2560, "bf16"),      # 2B-4T q, k, v
+               ((20, 0, 36, 100), 1008, "f32"),       # ragged, an empty matrix
+               ((8, 12, 4, 16), 28672, "bf16"),       # 256-lane teams
+               ((4, 8), 40000, "f32"),                # K > 32768: fallback
+               ((12, 4), 0, "bf16"),                  # K == 0
+               ((1024,), 4608, "bf16")]
+
+
+@pytest.mark.parametrize("Ns,K,dtype", GROUP_CASES)
+def test_quant_gemv_group(env, Ns, K, dtype):
+    torch, tq, oracle = env
+    say(f"quant_gemv_group {dtype} Ns={Ns} K={K}")
+    packs, refs = [], []
+    for i, N in enumerate(Ns):
+        codes = workloads.ternary_codes(N, K, seed=31 + 7 * i + N + K)
+        if N * K:
+            p, r = dev_packed(env, codes)
+        else:   # empty: nothing to pack on the device
+            p = torch.empty(N // 4, K, dtype=torch.uint8, device="cuda")
+            r = oracle.pack(codes)
+        packs.append(p)
+        refs.append(r)
+    scales = [workloads.tensor_scale(i) for i in range(len(Ns))]
+    if dtype == "bf16":
+        xh = workloads.activations_bf16(1, K, seed=K + 5, outliers=True)
+        x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).cuda()[0]
+    else:
+        xh = workloads.normal_f32(1, K, seed=K + 6, outliers=True)
+        x = torch.from_numpy(xh).cuda()[0]
+    accs = [torch.full((N,), 7, dtype=torch.int32, device="cuda") for N in Ns]
+    xq = torch.empty(K, dtype=torch.int8, device="cuda")
+    xs = torch.empty(1, dtype=torch.float32, device="cuda")
+    unit = torch.tensor([np.float32(1) / np.float32(127)], device="cuda")
+    ys = tq.tq_quant_gemv_group(x, packs, scales, acc=accs, xq=xq, x_scale=xs)
+    ysu = tq.tq_quant_gemv_group(x, packs, scales, y_scale=unit)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.act_quant(xh.reshape(1, K), dtype)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref[0])
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    u = unit.cpu().numpy()
+    for i, N in enumerate(Ns):
+        acc_ref, y32 = oracle.gemv(refs[i], scales[i], q_ref, s_ref, N)
+        np.testing.assert_array_equal(accs[i].cpu().numpy(), acc_ref[0], err_msg=f"acc {i}")
+        check_y(ys[i].cpu().numpy(), y32[0],
+                oracle.rescale(acc_ref, scales[i], s_ref, exact=True)[0])
+        _, y32u = oracle.gemv(refs[i], scales[i], q_ref, u, N)
+        check_y(ysu[i].cpu().numpy(), y32u[0],
+                oracle.rescale(acc_ref, scales[i], u, exact=True)[0])
+        # bit-identical to the single-matrix call
+        if N:
+            y1 = tq.tq_quant_gemv(x, packs[i], scales[i], y_scale=unit)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(y1.cpu().numpy().view(np.uint32),
+                                          ysu[i].cpu().numpy().view(np.uint32))
+
+
 @pytest.mark.parametrize("N,K", [(6912, 2560), (20, 48), (1028, 4608), (256, 28672),
                                  (8, 40000)])
 def test_quant_gate_up_relu2(env, N, K):
