@@ -273,3 +273,83 @@ def decode_chain(layers, h0_bf16, keep_stages: bool = False):
         h, dt = st["h"], "f32"
         stages.append(st if keep_stages else {"h": st["h"]})
     return h, stages
+
+
+# --------------------------------------------------------------------------
+# Absmean ternarization of bf16 weights (the step before packing).
+#
+# Page "1bit.systems" project README, section "read more": the project's
+# training runs use absmean quantization-aware training; page "Feature
+# request: BitNet 1.58-bit ternary inference on ROCm (gfx1151)", section
+# "Architecture": checkpoints come either as packed uint8 or as
+# pre-dequantized bf16.  The pages give no formula.  Reading used (the
+# BitNet b1.58 absmean rule, written so that every decision is exact):
+#   s   = RN32(mean_{n,k} |w[n,k]|)       (exact sum, one rounding)
+#   s'  = max(s, 1e-5f)
+#   inv = RN32(1 / s')
+#   c   = clamp(rne(RN32(w * inv)), -1, 1)
+# and s' is the weight scale (real weight = s' * c).
+# --------------------------------------------------------------------------
+from fractions import Fraction as _Fraction
+
+_F32_MIN_EXP = -126      # smallest normal binary32 exponent
+_F32_P = 24              # binary32 significand bits
+
+
+def rn32_fraction(v) -> np.float32:
+    """Round an exact rational to binary32, ties to even (IEEE 754
+    roundTiesToEven, gradual underflow); magnitudes above the largest finite
+    value are out of scope here (weights are finite bf16)."""
+    v = _Fraction(v)
+    if v == 0:
+        return np.float32(0.0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if _Fraction(2) ** e > a:
+        e -= 1
+    elif _Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = _Fraction(2) ** (max(e, _F32_MIN_EXP) - (_F32_P - 1))
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > _Fraction(1, 2) or (rem == _Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return np.float32(sign * float(fl * ulp))
+
+
+def abs_sum_bf16(w_bits) -> _Fraction:
+    """Exact sum of |w| over bf16 bit patterns (uint16/int16, any shape).
+    |w| = M * 2^(max(e,1) - 134) with e the 8-bit exponent field and M the
+    significand (hidden bit included for e >= 1); the sum is taken exactly
+    as an integer multiple of 2^-133, grouping equal exponents."""
+    b = np.asarray(w_bits).view(np.uint16).ravel().astype(np.int64)
+    e = (b >> 7) & 0xFF
+    if np.any(e == 0xFF):
+        raise OracleError("Inf/NaN weights are outside the contract")
+    m = (b & 0x7F) | np.where(e > 0, 0x80, 0)
+    total = 0
+    for ev in np.unique(e):
+        total += int(m[e == ev].sum(dtype=np.int64)) << (max(int(ev), 1) - 1)
+    return _Fraction(total, 1 << 133)
+
+
+def absmean_scale(w_bits) -> np.float32:
+    """s' = max(RN32(sum |w| / count), 1e-5f), exact sum, one rounding."""
+    n = np.asarray(w_bits).size
+    if n == 0:
+        return np.float32(1e-5)
+    s = rn32_fraction(abs_sum_bf16(w_bits) / n)
+    return max(s, np.float32(1e-5))
+
+
+def ternarize(w_bits):
+    """bf16 weights [N, K] -> (codes int8 [N, K] in {-1, 0, 1}, s')."""
+    s = absmean_scale(w_bits)
+    inv = np.float32(1.0) / s                      # RN32 division
+    # bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one
+    w = (np.asarray(w_bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    y = (w * inv).astype(np.float32)               # RN32 product
+    codes = np.clip(np.rint(y), -1, 1).astype(np.int8)
+    return codes, s
