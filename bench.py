@@ -25,8 +25,8 @@ Timing:
     between graph nodes, so it is an upper bound on the kernel duration
     that rocprofv3's kernel trace reports.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
-    gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64) and the
-    30-layer decode-step chain (graph-captured).
+    gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64), the absmean
+    ternarizer and the 30-layer decode-step chain (graph-captured).
   * cpu_baseline: the CPU oracle (plain C, one thread) on one step, repeated
     for about 10 s.
 Prints one JSON line on stdout; progress on stderr.
@@ -464,6 +464,32 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
             log(f"gemm_small M={M} {N}x{K}: {gemm[f'M{M}_{N}x{K}']}")
         del P
     rows["gemm_small"] = gemm
+
+    # absmean ternarizer (the step before packing), 70B-class [8192, 28672]:
+    # two passes over the bf16 weights (the exact mean precedes every code)
+    N, K = 8192, 28672
+    W = []
+    for c in range(2):
+        g = torch.Generator(device=dev).manual_seed(98000 + c)
+        W.append((torch.randn(N, K, generator=g, device=dev) * 0.02).to(torch.bfloat16))
+    pk = torch.empty(N // 4, K, dtype=torch.uint8, device=dev)
+    sw = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.TQ_TERNARIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    reps_t = 8
+
+    def ft(st):
+        for r in range(reps_t):
+            tq.tq_ternarize(W[(st + r) % 2], pk, sw, ws)
+    gs = [timer.graph(lambda s=s: ft(s)) for s in range(2)]
+    us = timer.time_graphs(gs, 4) * 1e3 / reps_t
+    tb = 2 * (2 * N * K) + N * K // 4
+    rows["ternarize_8192x28672"] = {
+        "us_per_call": round(us, 2),
+        "bf16_weight_GBs": round(2 * N * K / us / 1e3, 1),
+        "algo_GBs": round(tb / us / 1e3, 1),
+        "pct_hbm_peak": round(100 * tb / us / 1e3 / HBM_PEAK_GBS, 1)}
+    log(f"ternarize: {rows['ternarize_8192x28672']}")
+    del W, gs
 
     # a6: the 30-layer decode-step chain (2B-4T layers, M = 1), one graph
     layers = []

@@ -29,7 +29,7 @@ STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN",
 
 EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
            "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
-           "tq_quant_gemv_group", "tq_status_string")
+           "tq_quant_gemv_group", "tq_ternarize", "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
                                    p, p, p, p],
         # host arrays: packed**, w_scale*, N*, y**, acc** (ctypes arrays)
         "tq_quant_gemv_group": [p, i32, i32, p, p, p, i64, p, p, p, p, p, p],
+        "tq_ternarize": [p, i64, i64, p, p, p, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -300,6 +301,39 @@ def tq_quant_gemv_group(x, packed, w_scale, y=None, acc=None, xq=None,
         None if c_acc is None else ctypes.cast(c_acc, ctypes.c_void_p),
         _ptr(xq), _ptr(x_scale), _ptr(y_scale), _stream(stream)))
     return y
+
+
+TQ_TERNARIZE_WORKSPACE_BYTES = 4096
+_ws_cache = {}
+
+
+def tq_ternarize(w, packed=None, w_scale=None, workspace=None, stream=None):
+    """bf16 weights [N, K] -> (packed uint8 [N/4, K], w_scale fp32 [1]) by
+    the absmean rule (exact mean, one rounding).  The workspace (device,
+    >= TQ_TERNARIZE_WORKSPACE_BYTES) is cached per device when not given;
+    calls that may overlap on different streams must pass their own."""
+    torch = _torch()
+    if w.dtype != torch.bfloat16:
+        raise TypeError(f"w must be bfloat16, got {w.dtype}")
+    _need(w, "w", torch.bfloat16, w.device)
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    dev = w.device
+    packed = _out(packed, "packed", (N // 4, K), torch.uint8, dev)
+    w_scale = _out(w_scale, "w_scale", (1,), torch.float32, dev)
+    if workspace is None:
+        key = (dev.type, dev.index)
+        workspace = _ws_cache.get(key)
+        if workspace is None:
+            workspace = torch.empty(TQ_TERNARIZE_WORKSPACE_BYTES, dtype=torch.uint8,
+                                    device=dev)
+            _ws_cache[key] = workspace
+    elif workspace.numel() * workspace.element_size() < TQ_TERNARIZE_WORKSPACE_BYTES:
+        raise ValueError("workspace too small")
+    _check("tq_ternarize", lib.tq_ternarize(_ptr(w), N, K, _ptr(packed), _ptr(w_scale),
+                                            _ptr(workspace), _stream(stream)))
+    return packed, w_scale
 
 
 def tq_quant_gate_up_relu2(x, packed_gate, s_gate, packed_up, s_up, h=None,

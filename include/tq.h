@@ -212,6 +212,31 @@ TQ_API tq_status tq_quant_gemv_group(const void *x, tq_dtype xt, int32_t count,
                                      float *x_scale, const float *y_scale,
                                      hipStream_t stream);
 
+/*
+ * tq_ternarize -- bf16 weights -> packed ternary codes and the weight scale,
+ * by the absmean rule (the step before the GEMV for checkpoints that come as
+ * pre-dequantized bf16: [ISSUE] "Architecture"; absmean quantization is
+ * named on the "1bit.systems" README, "read more").  The pages give no
+ * formula; this library's reading:
+ *   s' = max(RN32(mean_{n,k} |w[n,k]|), 1e-5)  -- the sum is exact, rounded
+ *        once, so the result does not depend on summation order;
+ *   c  = clamp(rne(RN32(w * RN32(1/s'))), -1, 1), packed as tq_pack does.
+ *   w          bf16 [N,K] device, 16-B aligned; finite values.
+ *   packed     uint8 [N/4,K] device output, 16-B aligned.
+ *   w_scale    fp32 [1] device output: s' (pass it by value to the GEMV calls
+ *              after reading it back once).
+ *   workspace  device scratch of at least TQ_TERNARIZE_WORKSPACE_BYTES bytes,
+ *              8-B aligned, any contents; the call clears what it uses.  Calls
+ *              that overlap in time must not share one workspace.
+ * N % 4 == 0, K % 16 == 0, N*K <= 2^31 - 1.  With N*K == 0 only w_scale is
+ * written (1e-5).  Four launches (clear, exact |w| histogram, final
+ * rounding, quantize + pack).
+ */
+#define TQ_TERNARIZE_WORKSPACE_BYTES 4096
+TQ_API tq_status tq_ternarize(const void *w, int64_t N, int64_t K,
+                              uint8_t *packed, float *w_scale, void *workspace,
+                              hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 TQ_API const char *tq_status_string(tq_status status);
 

@@ -33,7 +33,7 @@ def test_header_declares_the_calls():
     assert set(names) == {"tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
                           "tq_gate_up_relu2", "tq_quant_gemv",
                           "tq_quant_gate_up_relu2", "tq_quant_gemv_group",
-                          "tq_status_string"}
+                          "tq_ternarize", "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -158,6 +158,22 @@ def test_quant_gemv_group_validation(tq):
     assert call(xq=None) == NULL
 
 
+def test_ternarize_validation(tq):
+    f = tq.lib.tq_ternarize
+    assert f(A, 6, 16, A, A, A, None) == SHAPE
+    assert f(A, 8, 24, A, A, A, None) == SHAPE
+    assert f(A, -4, 16, A, A, A, None) == SHAPE
+    assert f(A, 1 << 20, 1 << 12, A, A, A, None) == SHAPE     # N*K > 2^31 - 1
+    assert f(A, 8, 16, A, None, A, None) == NULL
+    assert f(A, 8, 16, A, A, None, None) == NULL
+    assert f(None, 8, 16, A, A, A, None) == NULL
+    assert f(A, 8, 16, None, A, A, None) == NULL
+    assert f(MIS, 8, 16, A, A, A, None) == ALIGN
+    assert f(A, 8, 16, MIS, A, A, None) == ALIGN
+    assert f(A, 8, 16, A, ODD, A, None) == ALIGN
+    assert f(A, 8, 16, A, A, P(0x10004), None) == ALIGN
+
+
 def test_pack_validation(tq):
     f = tq.lib.tq_pack
     assert f(A, 5, 16, A, None) == SHAPE
@@ -181,6 +197,7 @@ def test_no_device_is_reported(tq):
     assert gemv(tq) == DEVICE
     assert tq.lib.tq_act_quant(A, 0, 1, 64, A, A, None) == DEVICE
     assert tq.lib.tq_pack(A, 8, 16, A, None) == DEVICE
+    assert tq.lib.tq_ternarize(A, 8, 16, A, A, A, None) == DEVICE
     assert tq.lib.tq_gemm_small(A, 0.02, A, A, 4, 64, 64, A, None, None) == DEVICE
     assert tq.lib.tq_quant_gemv(A, 0, A, 0.02, 64, 64, A, None, A, A, None,
                                 None) == DEVICE

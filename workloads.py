@@ -122,3 +122,11 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def activations_bf16(M: int, K: int, seed: int, outliers: bool = False) -> np.ndarray:
     """Synthetic bf16 activations [M, K] as uint16 bit patterns."""
     return to_bf16_bits(normal_f32(M, K, seed, outliers))
+
+
+def weights_bf16(N: int, K: int, seed: int, sigma: float = 0.02) -> np.ndarray:
+    """Synthetic pre-dequantized weights [N, K]: fp32 N(0, sigma^2) rounded
+    to bf16 (uint16 bit patterns), the input of the absmean ternarizer."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(sigma)
+    return to_bf16_bits(w)
