@@ -14,34 +14,62 @@
 //   c   = clamp(rne(RN32(w * inv)), -1, 1), packed as tq_pack does.
 //
 // Exact sum: |w| = M * 2^(max(e,1) - 134) for the 8-bit exponent field e
-// and the significand M (hidden bit included for e >= 1).  A histogram of
-// M-sums per exponent (integers, so any order gives the same totals) is
-// built with LDS atomics per block and 64-bit global atomics across blocks;
-// one thread then combines the 255 totals as a 384-bit integer, divides by
-// N*K and rounds once.
+// and the significand M (hidden bit included for e >= 1).  Integer sums per
+// exponent (so any order gives the same totals) are built per block, in
+// registers for the common exponents and in LDS for the rest, and merged
+// with 64-bit global atomics; a tree of 384-bit integers then combines them
+// and one thread divides by N*K and rounds once.
 #include "tq_device.h"
 #include "tq_host.h"
 
 namespace tq {
 namespace {
 
-constexpr int kHistCopies = 16;  // LDS copies of the histogram (lane % 16)
 constexpr int kWsInvOffset = 2048;  // workspace: u64 bucket[256], then inv
+constexpr int kWindow = 24;         // binades below a block's top exponent
+                                    // summed in per-thread registers
 
 __global__ __launch_bounds__(256) void ws_clear_kernel(unsigned long long *ws) {
   ws[threadIdx.x] = 0ull;  // 256 buckets (and the 2 KB that follow are
                            // written before they are read)
 }
 
+// bucket[e] receives integers B with sum|w| = sum_e B[e] * 2^(max(e,1)-134).
+// Weights with exponent field e in [R - kWindow, R] (R: the largest exponent
+// among the block's first loads) are summed exactly in a 64-bit register as
+// M << (e - (R - kWindow)) and enter bucket[R - kWindow] once per thread
+// (M < 2^8, shift <= 24: a term is < 2^32, so a thread's sum and any
+// bucket over <= 2^31 weights stay < 2^63).  The rest (rare for real
+// weights) go to an LDS histogram of significand sums.
 __global__ __launch_bounds__(256) void absmean_hist_kernel(
     const u32x4 *__restrict__ w, int64_t pieces, unsigned long long *bucket) {
-  __shared__ unsigned part[kHistCopies][256];
-  for (int t = threadIdx.x; t < kHistCopies * 256; t += 256) (&part[0][0])[t] = 0u;
+  __shared__ unsigned long long h64[256];
+  __shared__ unsigned h32[256];
+  __shared__ unsigned top_lds[256 / kWave];
+  h64[threadIdx.x] = 0ull;
+  h32[threadIdx.x] = 0u;
+  const int64_t first = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  unsigned emax = 0;
+  if (first < pieces) {
+    const u32x4 v = w[first];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const unsigned e0 = (v[d] >> 7) & 0xffu, e1 = (v[d] >> 23) & 0xffu;
+      emax = max(emax, max(e0, e1));
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) emax = max(emax, (unsigned)__shfl_xor((int)emax, off, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) top_lds[threadIdx.x / kWave] = emax;
   __syncthreads();
-  unsigned *mine = part[threadIdx.x % kHistCopies];
-  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < pieces;
-       p += (int64_t)gridDim.x * blockDim.x) {
-    const u32x4 v = w[p];  // 8 bf16
+  unsigned R = top_lds[0];
+#pragma unroll
+  for (int i = 1; i < 256 / kWave; ++i) R = max(R, top_lds[i]);
+  // Window only over normal exponents (R - kWindow >= 1 keeps the scaling
+  // of bucket[R - kWindow] the plain 2^(e-134)).
+  const unsigned lo = R > kWindow ? R - kWindow : 256u;  // 256: no window
+  unsigned long long acc = 0ull;
+  auto add_piece = [&](const u32x4 &v) {  // 8 bf16
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -49,58 +77,77 @@ __global__ __launch_bounds__(256) void absmean_hist_kernel(
         const uint32_t b = (v[d] >> (16 * h)) & 0xffffu;
         const uint32_t e = (b >> 7) & 0xffu;
         const uint32_t m = (b & 0x7fu) | (e ? 0x80u : 0u);
-        if (m) atomicAdd(&mine[e], m);
+        if (e >= lo && e <= R) {
+          acc += (unsigned long long)m << (e - lo);
+        } else if (m) {
+          atomicAdd(&h32[e], m);  // < 2^32: at most 2^24 weights per block
+        }
       }
-  }
+  };
+  for (int64_t p = first; p < pieces; p += stride) add_piece(w[p]);
+  if (acc) atomicAdd(&h64[lo], acc);
   __syncthreads();
-  // Per copy and bucket at most (elements per block / 16) * 255 < 2^32 for
-  // the grid sizes launched (the host caps elements per block at 2^24).
-  unsigned long long total = 0;
-#pragma unroll
-  for (int c = 0; c < kHistCopies; ++c) total += part[c][threadIdx.x];
+  const unsigned long long total = h64[threadIdx.x] + h32[threadIdx.x];
   if (total) atomicAdd(&bucket[threadIdx.x], total);
 }
 
-// t[i..] += v (v < 2^64), carries propagated up to limb L-1.
-template <int L>
-__device__ void add_at(uint32_t (&t)[L], int i, uint64_t v) {
-  uint64_t carry = v;
-  for (; carry && i < L; ++i) {
-    const uint64_t s = (uint64_t)t[i] + (carry & 0xffffffffull);
-    t[i] = (uint32_t)s;
-    carry = (carry >> 32) + (s >> 32);
-  }
-}
+constexpr int kLimbs = 12;  // 384-bit integers
 
-__global__ __launch_bounds__(64) void absmean_final_kernel(
+// Final rounding.  T' = sum_e bucket[e] * 2^(max(e,1) - 1 + 64), so that
+// sum|w| = T' * 2^-197; bucket < 2^63 and the shift <= 317 give T' < 2^381.
+// Every thread turns one bucket into a 12-limb integer, a tree in LDS sums
+// them, and thread 0 divides by the count and rounds once.
+__global__ __launch_bounds__(256) void absmean_final_kernel(
     const unsigned long long *bucket, uint32_t count, float *w_scale,
     float *inv_out) {
-  if (threadIdx.x != 0) return;
-  // T' = sum_e bucket[e] * 2^(max(e,1) - 1 + 64): sum|w| = T' * 2^-197.
-  // bucket < 2^40 and the shift <= 317, so T' < 2^358 fits 12 limbs.
-  constexpr int L = 12;
-  uint32_t t[L];
+  __shared__ uint32_t limbs[256][kLimbs + 1];  // +1: bank spread
+  {
+    uint32_t *t = limbs[threadIdx.x];
 #pragma unroll
-  for (int i = 0; i < L; ++i) t[i] = 0u;
-  for (int e = 0; e < 255; ++e) {  // e = 255 (Inf/NaN) is out of contract
-    const uint64_t b = bucket[e];
-    if (!b) continue;
-    const int sh = (e > 0 ? e : 1) - 1 + 64;
-    const int limb = sh >> 5, bit = sh & 31;
-    add_at(t, limb, (uint64_t)(uint32_t)b << bit);
-    add_at(t, limb + 1, (uint64_t)(uint32_t)(b >> 32) << bit);
+    for (int i = 0; i < kLimbs; ++i) t[i] = 0u;
+    const int e = threadIdx.x;
+    const uint64_t b = e < 255 ? bucket[e] : 0ull;  // 255: Inf/NaN, outside
+    if (b) {
+      const int sh = (e > 0 ? e : 1) - 1 + 64;
+      const int limb = sh >> 5, bit = sh & 31;
+      // b << bit spans three limbs (b < 2^63, bit < 32).
+      const uint64_t lo = (uint64_t)(uint32_t)b << bit;
+      const uint64_t hi = (uint64_t)(uint32_t)(b >> 32) << bit;
+      const uint64_t mid = (lo >> 32) + (hi & 0xffffffffull);
+      t[limb] = (uint32_t)lo;
+      t[limb + 1] = (uint32_t)mid;
+      t[limb + 2] = (uint32_t)((hi >> 32) + (mid >> 32));
+    }
   }
+  __syncthreads();
+  for (int half = 128; half >= 1; half >>= 1) {
+    if ((int)threadIdx.x < half) {
+      uint32_t *a = limbs[threadIdx.x];
+      const uint32_t *c = limbs[threadIdx.x + half];
+      uint64_t carry = 0;
+#pragma unroll
+      for (int i = 0; i < kLimbs; ++i) {
+        const uint64_t s = (uint64_t)a[i] + c[i] + carry;
+        a[i] = (uint32_t)s;
+        carry = s >> 32;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  const uint32_t *t = limbs[0];
   float s = 0.0f;
   if (count > 0) {
     // q = floor(T' / count), rem = T' mod count.
-    uint32_t q[L];
+    uint32_t q[kLimbs];
     uint64_t rem = 0;
-    for (int i = L - 1; i >= 0; --i) {
+#pragma unroll
+    for (int i = kLimbs - 1; i >= 0; --i) {
       const uint64_t cur = (rem << 32) | t[i];
       q[i] = (uint32_t)(cur / count);
       rem = cur % count;
     }
-    int top_limb = L - 1;
+    int top_limb = kLimbs - 1;
     while (top_limb >= 0 && q[top_limb] == 0u) --top_limb;
     if (top_limb >= 0) {
       // q >= 2^64 / 2^31 whenever T' > 0, so it has >= 34 significant bits.
@@ -112,8 +159,14 @@ __global__ __launch_bounds__(64) void absmean_final_kernel(
         uint32_t top = 0;
         for (int k = 23; k >= 0; --k) top = (top << 1) | bit_at(shift + k);
         const uint32_t round = bit_at(shift - 1);
+        // sticky: any set bit below position shift - 1, or a remainder
         bool sticky = rem != 0;
-        for (int pos = 0; pos < shift - 1 && !sticky; ++pos) sticky = bit_at(pos);
+        const int below = shift - 1;  // bits [0, below) of q
+        for (int i = 0; i < kLimbs && 32 * i < below; ++i) {
+          const int nb = below - 32 * i;
+          const uint32_t mask = nb >= 32 ? 0xffffffffu : ((1u << nb) - 1u);
+          sticky |= (q[i] & mask) != 0u;
+        }
         if (round && (sticky || (top & 1u))) ++top;
         if (top == (1u << 24)) {
           top >>= 1;
@@ -188,7 +241,7 @@ extern "C" tq_status tq_ternarize(const void *w, int64_t N, int64_t K,
                              stream, static_cast<const u32x4 *>(w), pieces, ws))
       return s;
   }
-  if (tq_status s = launch(absmean_final_kernel, dim3(1), dim3(64), 0, stream,
+  if (tq_status s = launch(absmean_final_kernel, dim3(1), dim3(256), 0, stream,
                            static_cast<const unsigned long long *>(ws),
                            (uint32_t)count, w_scale, inv))
     return s;
