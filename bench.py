@@ -135,6 +135,73 @@ def cpu_baseline(budget_s=10.0):
                        f"{os.cpu_count()} host cores visible)")}
 
 
+def cpu_rows(budget_s=3.0):
+    """The CPU oracle on a bounded sample of each hot-path row (one thread):
+    per row, repeated calls for about `budget_s` seconds; weight GB/s (or
+    tokens/s for the chain) of the oracle as it stands."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    def timed(fn):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return reps, el
+
+    out = {}
+    H, I = workloads.HIDDEN, workloads.INTERMEDIATE
+    # a1 act-quant, M = 1, K = 6912
+    xb = workloads.activations_bf16(1, I, seed=501)
+    reps, el = timed(lambda: oracle.act_quant(xb, "bf16"))
+    out["act_quant_M1_K6912"] = {"us_per_call": round(el / reps * 1e6, 1),
+                                 "sample": f"{reps} calls"}
+    # a4 gate/up + relu^2 M = 1 [6912, 2560] x 2
+    pg = oracle.pack(workloads.ternary_codes(I, H, seed=502))
+    pu = oracle.pack(workloads.ternary_codes(I, H, seed=503))
+    q, sx = oracle.act_quant(workloads.activations_bf16(1, H, seed=504), "bf16")
+    reps, el = timed(lambda: oracle.gate_up_relu2(pg, 0.024, pu, 0.025, q, sx, I))
+    out["gate_up_relu2_M1_6912x2560"] = {
+        "weight_GBs": round(2 * weight_bytes(I, H) * reps / el / 1e9, 4),
+        "sample": f"{reps} calls"}
+    # a5 small-batch GEMM, M = 16, [2560, 6912]
+    pd = oracle.pack(workloads.ternary_codes(H, I, seed=505))
+    q16, s16 = oracle.act_quant(workloads.activations_bf16(16, I, seed=506), "bf16")
+    reps, el = timed(lambda: oracle.gemv(pd, 0.02, q16, s16, H))
+    out["gemm_small_M16_2560x6912"] = {
+        "weight_GBs": round(weight_bytes(H, I) * reps / el / 1e9, 4),
+        "int8_GOPS": round(2 * 16 * H * I * reps / el / 1e9, 3),
+        "sample": f"{reps} calls"}
+    # a6 decode chain: 2 layers of the 30 (per-layer cost x 30 = per token)
+    layers = []
+    for l in range(2):
+        layer = {}
+        for name, (N, K) in workloads.LAYER_2B4T.items():
+            t = workloads.TENSOR_INDEX[name]
+            layer[name] = (oracle.pack(workloads.ternary_codes(
+                N, K, seed=workloads.seed_for(2, t, l))), workloads.tensor_scale(t), N)
+        layers.append(layer)
+    h0 = workloads.activations_bf16(1, H, seed=507, outliers=True)
+    reps, el = timed(lambda: oracle.decode_chain(layers, h0))
+    per_layer = el / reps / 2
+    out["decode_chain_30x2b4t"] = {
+        "us_per_token": round(per_layer * workloads.CHAIN_LAYERS * 1e6, 1),
+        "tokens_per_s": round(1 / (per_layer * workloads.CHAIN_LAYERS), 3),
+        "sample": f"{reps} passes over 2 layers, scaled to 30"}
+    # next-1 absmean ternarizer on [2560, 6912] bf16 weights
+    wb = workloads.weights_bf16(H, I, seed=508)
+    reps, el = timed(lambda: oracle.ternarize(wb))
+    out["ternarize_2560x6912"] = {
+        "bf16_weight_GBs": round(2 * H * I * reps / el / 1e9, 4),
+        "sample": f"{reps} calls"}
+    out["cores"] = 1
+    return out
+
+
 class Timer:
     """Graph-captured launch sequences timed with HIP events."""
 
@@ -297,6 +364,10 @@ def main():
         rows = measure_rows(torch, tq, workloads, timer, dev, R, per_shape)
 
     cpu = None if args.no_cpu else cpu_baseline()
+    if cpu is not None and not args.no_rows:
+        log("cpu oracle rows")
+        cpu["rows"] = cpu_rows()
+        log(f"cpu rows: {cpu['rows']}")
 
     out = {
         "metric": METRIC,
@@ -389,7 +460,7 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
         return timer.time_graphs(gs, reps) * 1e3 / R
 
     # a1: act_quant on bf16 rows (input cache-resident: it is reused)
-    aq = {}
+    aq = {}  # us per launch; bytes 2K in + K + 4 out (latency bound)
     for K in (2560, 6912, 8192, 28672):
         xb = workloads.activations_bf16(1, K, seed=K)
         xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -417,7 +488,8 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
     us = loop_us(fq, len(P))
     rows["gemv_q_proj_2560x2560"] = {
         "us_per_launch": round(us, 3),
-        "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1)}
+        "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1),
+        "pct_hbm_peak": round(100 * algo_bytes(N, K) / us / 1e3 / HBM_PEAK_GBS, 1)}
     log(f"gemv q_proj: {rows['gemv_q_proj_2560x2560']}")
     del P
 
@@ -437,7 +509,9 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
     us = loop_us(fg, len(pg))
     rows["gate_up_relu2_M1_6912x2560"] = {
         "us_per_launch": round(us, 3),
-        "weight_GBs": round(2 * weight_bytes(N, K) / us / 1e3, 1)}
+        "weight_GBs": round(2 * weight_bytes(N, K) / us / 1e3, 1),
+        "pct_hbm_peak": round(100 * (2 * weight_bytes(N, K) + K + 4 + 4 * N)
+                              / us / 1e3 / HBM_PEAK_GBS, 1)}
     log(f"gate_up: {rows['gate_up_relu2_M1_6912x2560']}")
     del pg, pu
 
@@ -459,6 +533,7 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
             gemm[f"M{M}_{N}x{K}"] = {
                 "us_per_launch": round(us, 3),
                 "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1),
+                "pct_hbm_peak": round(100 * algo_bytes(N, K, M) / us / 1e3 / HBM_PEAK_GBS, 1),
                 "int8_TOPS": round(ops / us / 1e6, 2),
                 "mfma_frac": round(ops / us / 1e6 / INT8_MFMA_PEAK_TOPS, 4)}
             log(f"gemm_small M={M} {N}x{K}: {gemm[f'M{M}_{N}x{K}']}")
@@ -515,6 +590,7 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
             "us_per_token": round(ms * 1e3, 2),
             "tokens_per_s": round(1e3 / ms, 1),
             "weight_GBs": round(total / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
             "launches_per_token": launches * workloads.CHAIN_LAYERS}
         log(f"{key}: {rows[key]}")
         del g, chain
