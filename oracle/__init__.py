@@ -353,3 +353,38 @@ def ternarize(w_bits):
     y = (w * inv).astype(np.float32)               # RN32 product
     codes = np.clip(np.rint(y), -1, 1).astype(np.int8)
     return codes, s
+
+
+# --------------------------------------------------------------------------
+# Split-KV (flash-decoding) attention at decode: the reference result.
+#
+# Page "1bit.systems" project README, section "honest numbers": split-KV
+# Flash-Decoding attention at L = 2048; page "Feature request: BitNet 1.58-bit
+# ternary inference on ROCm (gfx1151)", section "Weight mapping": 20 query
+# heads, 5 KV heads, head_dim 128 (grouped-query attention).  The pages give
+# no formula or precision; reading used (standard scaled dot-product
+# attention for one query token over L cached tokens, no mask):
+#   s[h,t] = scale * sum_d q[h,d] * k[t,g,d],   g = h // (H / Hkv)
+#   o[h,:] = sum_t softmax_t(s[h,:]) * v[t,g,:]
+# q is fp32 [H, D]; k and v are bf16 [L, Hkv, D] (a token-major KV cache).
+# The oracle evaluates this definition in float64 (exact bf16 widening).
+# --------------------------------------------------------------------------
+def attn_decode(q, k_bits, v_bits, scale) -> np.ndarray:
+    """float64 [H, D] attention output of one query token (see above)."""
+    q = np.asarray(q, np.float32)
+    k_bits = np.asarray(k_bits).view(np.uint16)
+    v_bits = np.asarray(v_bits).view(np.uint16)
+    H, D = q.shape
+    L, Hkv, Dk = k_bits.shape
+    if Dk != D or v_bits.shape != k_bits.shape or L < 1 or H % Hkv:
+        raise OracleError("bad attention shapes")
+    widen = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    k, v = widen(k_bits), widen(v_bits)
+    G = H // Hkv
+    out = np.empty((H, D), np.float64)
+    for h in range(H):
+        g = h // G
+        s = (k[:, g, :] @ q[h].astype(np.float64)) * float(np.float32(scale))
+        w = np.exp(s - s.max())
+        out[h] = (w @ v[:, g, :]) / w.sum()
+    return out
