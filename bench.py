@@ -26,7 +26,8 @@ Timing:
     that rocprofv3's kernel trace reports.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
     gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64), the absmean
-    ternarizer and the 30-layer decode-step chain (graph-captured).
+    ternarizer, split-KV decode attention and the 30-layer decode-step chain
+    (graph-captured).
   * cpu_baseline: the CPU oracle (plain C, one thread) on one step, repeated
     for about 10 s.
 Prints one JSON line on stdout; progress on stderr.
@@ -198,6 +199,14 @@ def cpu_rows(budget_s=3.0):
     out["ternarize_2560x6912"] = {
         "bf16_weight_GBs": round(2 * H * I * reps / el / 1e9, 4),
         "sample": f"{reps} calls"}
+    # next-4 decode attention, 2B-4T heads, L = 2048
+    rng = np.random.default_rng(509)
+    qa = rng.standard_normal((20, 128)).astype(np.float32)
+    kb = (rng.standard_normal((2048, 5, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vb = (rng.standard_normal((2048, 5, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    reps, el = timed(lambda: oracle.attn_decode(qa, kb, vb, np.float32(128 ** -0.5)))
+    out["attn_decode_L2048"] = {"us_per_call": round(el / reps * 1e6, 1),
+                                "sample": f"{reps} calls"}
     out["cores"] = 1
     return out
 
@@ -565,6 +574,34 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
         "pct_hbm_peak": round(100 * tb / us / 1e3 / HBM_PEAK_GBS, 1)}
     log(f"ternarize: {rows['ternarize_8192x28672']}")
     del W, gs
+
+    # next-4: split-KV decode attention, 2B-4T heads (20 q, 5 kv, D = 128),
+    # bf16 KV cache pools of >= 640 MB so repeats are not served from cache
+    attn = {}
+    H, Hkv, D = 20, 5, 128
+    qa = torch.randn(H, D, device=dev, dtype=torch.float32)
+    oa = torch.empty(H, D, device=dev, dtype=torch.float32)
+    wsa = torch.empty(tq.attn_workspace_bytes(H, D), dtype=torch.uint8, device=dev)
+    for L in (2048, 8192, 32768):
+        kv_bytes = 2 * L * Hkv * D * 2
+        copies = max(4, -(-(640 << 20) // kv_bytes))
+        g = torch.Generator(device=dev).manual_seed(99000 + L)
+        KV = [(torch.randn(L, Hkv, D, generator=g, device=dev).to(torch.bfloat16),
+               torch.randn(L, Hkv, D, generator=g, device=dev).to(torch.bfloat16))
+              for _ in range(copies)]
+
+        def fa(st, KV=KV):
+            for r in range(R):
+                kk, vv = KV[(st + r) % len(KV)]
+                tq.tq_attn_decode(qa, kk, vv, out=oa, workspace=wsa)
+        us = loop_us(fa, len(KV))
+        ab = kv_bytes + 2 * H * D * 4
+        attn[f"L{L}"] = {"us_per_call": round(us, 3),
+                         "algo_GBs": round(ab / us / 1e3, 1),
+                         "pct_hbm_peak": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 1)}
+        log(f"attn L={L}: {attn[f'L{L}']}")
+        del KV
+    rows["attn_decode_2b4t_heads"] = attn
 
     # a6: the 30-layer decode-step chain (2B-4T layers, M = 1), one graph
     layers = []

@@ -29,7 +29,8 @@ STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN",
 
 EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
            "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
-           "tq_quant_gemv_group", "tq_ternarize", "tq_status_string")
+           "tq_quant_gemv_group", "tq_ternarize", "tq_attn_decode",
+           "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -58,6 +59,7 @@ def _load() -> ctypes.CDLL:
         # host arrays: packed**, w_scale*, N*, y**, acc** (ctypes arrays)
         "tq_quant_gemv_group": [p, i32, i32, p, p, p, i64, p, p, p, p, p, p],
         "tq_ternarize": [p, i64, i64, p, p, p, p],
+        "tq_attn_decode": [p, p, p, i64, i64, i64, i64, f32, p, p, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -334,6 +336,40 @@ def tq_ternarize(w, packed=None, w_scale=None, workspace=None, stream=None):
     _check("tq_ternarize", lib.tq_ternarize(_ptr(w), N, K, _ptr(packed), _ptr(w_scale),
                                             _ptr(workspace), _stream(stream)))
     return packed, w_scale
+
+
+def attn_workspace_bytes(H: int, D: int) -> int:
+    return H * 64 * (D + 2) * 8
+
+
+def tq_attn_decode(q, k_cache, v_cache, scale=None, out=None, workspace=None,
+                   stream=None):
+    """Attention of one query token: q fp32 [H, D], k/v bf16 [L, Hkv, D] ->
+    out fp32 [H, D] (fp64 inside, one rounding).  scale defaults to
+    1/sqrt(D) rounded to fp32.  The workspace is allocated when not given."""
+    torch = _torch()
+    _need(q, "q", torch.float32)
+    dev = q.device
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    if q.dim() != 2 or k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
+        raise ValueError("need q [H, D] and k/v [L, Hkv, D]")
+    H, D = q.shape
+    L, Hkv, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head dims differ")
+    if scale is None:
+        scale = ctypes.c_float(1.0 / math.sqrt(D)).value
+    out = _out(out, "out", (H, D), torch.float32, dev)
+    need = attn_workspace_bytes(H, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small")
+    _check("tq_attn_decode", lib.tq_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), H, Hkv, D, L, float(scale),
+        _ptr(out), _ptr(workspace), _stream(stream)))
+    return out
 
 
 def tq_quant_gate_up_relu2(x, packed_gate, s_gate, packed_up, s_up, h=None,

@@ -55,6 +55,7 @@
 #ifndef TQ_H
 #define TQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -236,6 +237,30 @@ TQ_API tq_status tq_quant_gemv_group(const void *x, tq_dtype xt, int32_t count,
 TQ_API tq_status tq_ternarize(const void *w, int64_t N, int64_t K,
                               uint8_t *packed, float *w_scale, void *workspace,
                               hipStream_t stream);
+
+/*
+ * tq_attn_decode -- attention of one query token over a KV cache, split
+ * over the cache (flash-decoding; [README] "honest numbers" names split-KV
+ * Flash-Decoding at L = 2048; [ISSUE] "Weight mapping": 20 query heads,
+ * 5 KV heads, head_dim 128).  The pages give no formula; this library's:
+ *   s[h,t] = scale * sum_d q[h,d] k[t,g,d],   g = h / (H/Hkv)
+ *   out[h,:] = sum_t softmax_t(s[h,:]) v[t,g,:]
+ * evaluated in fp64 (exact widening of the inputs) and rounded once to fp32;
+ * the summation order is fixed, so identical calls give identical bits.
+ *   q          fp32 [H, D] device, 16-B aligned.
+ *   k_cache, v_cache  bf16 [L, Hkv, D] device (token-major), 16-B aligned.
+ *   out        fp32 [H, D] device output.
+ *   workspace  device scratch of TQ_ATTN_WORKSPACE_BYTES(H, D) bytes, 8-B
+ *              aligned, any contents (per-split partial results); calls that
+ *              overlap in time must not share one workspace.
+ * H % Hkv == 0 with H/Hkv in {1, 2, 4, 8}; D in {64, 128}; 1 <= L <= 131072.
+ * Two launches (split pass, combine).
+ */
+#define TQ_ATTN_WORKSPACE_BYTES(H, D) ((size_t)(H) * 64u * ((size_t)(D) + 2u) * 8u)
+TQ_API tq_status tq_attn_decode(const float *q, const void *k_cache,
+                                const void *v_cache, int64_t H, int64_t Hkv,
+                                int64_t D, int64_t L, float scale, float *out,
+                                void *workspace, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 TQ_API const char *tq_status_string(tq_status status);

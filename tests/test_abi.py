@@ -33,7 +33,7 @@ def test_header_declares_the_calls():
     assert set(names) == {"tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
                           "tq_gate_up_relu2", "tq_quant_gemv",
                           "tq_quant_gate_up_relu2", "tq_quant_gemv_group",
-                          "tq_ternarize", "tq_status_string"}
+                          "tq_ternarize", "tq_attn_decode", "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -174,6 +174,22 @@ def test_ternarize_validation(tq):
     assert f(A, 8, 16, A, A, P(0x10004), None) == ALIGN
 
 
+def test_attn_decode_validation(tq):
+    f = tq.lib.tq_attn_decode
+    #        q  k  v   H  Hkv  D    L   scale  out ws  stream
+    assert f(A, A, A, 20, 3, 128, 16, 0.1, A, A, None) == SHAPE      # H % Hkv
+    assert f(A, A, A, 48, 4, 128, 16, 0.1, A, A, None) == SHAPE      # group 12
+    assert f(A, A, A, 20, 5, 96, 16, 0.1, A, A, None) == SHAPE       # D
+    assert f(A, A, A, 20, 5, 128, 0, 0.1, A, A, None) == SHAPE       # L = 0
+    assert f(A, A, A, 20, 5, 128, 131073, 0.1, A, A, None) == SHAPE
+    assert f(None, A, A, 20, 5, 128, 16, 0.1, A, A, None) == NULL
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, A, None, None) == NULL
+    assert f(MIS, A, A, 20, 5, 128, 16, 0.1, A, A, None) == ALIGN
+    assert f(A, MIS, A, 20, 5, 128, 16, 0.1, A, A, None) == ALIGN
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, ODD, A, None) == ALIGN
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, A, P(0x10004), None) == ALIGN
+
+
 def test_pack_validation(tq):
     f = tq.lib.tq_pack
     assert f(A, 5, 16, A, None) == SHAPE
@@ -198,6 +214,7 @@ def test_no_device_is_reported(tq):
     assert tq.lib.tq_act_quant(A, 0, 1, 64, A, A, None) == DEVICE
     assert tq.lib.tq_pack(A, 8, 16, A, None) == DEVICE
     assert tq.lib.tq_ternarize(A, 8, 16, A, A, A, None) == DEVICE
+    assert tq.lib.tq_attn_decode(A, A, A, 20, 5, 128, 16, 0.1, A, A, None) == DEVICE
     assert tq.lib.tq_gemm_small(A, 0.02, A, A, 4, 64, 64, A, None, None) == DEVICE
     assert tq.lib.tq_quant_gemv(A, 0, A, 0.02, 64, 64, A, None, A, A, None,
                                 None) == DEVICE

@@ -1,0 +1,126 @@
+"""GPU parity of tq_attn_decode against the float64 oracle, at the 2B-4T
+head layout (20 query heads, 5 KV heads, D = 128) for L from 1 to 32768
+(ragged chunk tails included), the other group sizes and D = 64, peaked
+softmax, exact cases (one token: out == v; identical keys), and bitwise
+determinism across calls.
+
+Tolerance (derived from the kernel's fp32 arithmetic, per head h):
+  E   = gamma(13) * scale * max_t sum_d |q[h,d] k[t,d]|   (score error: an
+        8-term FMA chain, a 16-lane tree, the scale product)
+  rho = 2E + u * max_t |s_t - m| + 2^-22                 (relative weight
+        error: scores, the subtraction, expf within 2 ulp)
+  |out - o| <= 2 max|v| rho + gamma(dN) max|v| + gamma(dD) |o| + ulp32(o)
+with gamma(n) = n u / (1 - n u), u = 2^-24, dN / dD the summation depths of
+the numerator / denominator (tokens per lane, shuffle and wave trees, the
+fp64 merge of the splits is exact to well below u).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import bit_gemv_tq_amd as tq
+    import oracle
+    return torch, tq, oracle
+
+
+def make(L, H, Hkv, D, seed, kscale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, D)).astype(np.float32)
+    kf = (rng.standard_normal((L, Hkv, D)) * kscale).astype(np.float32)
+    vf = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    tobf = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
+    return q, tobf(kf), tobf(vf)
+
+
+def ulp32(x):
+    a = np.abs(x).astype(np.float32)
+    return (np.nextafter(a, np.float32(np.inf)) - a).astype(np.float64)
+
+
+U = 2.0 ** -24
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+def bound(q, k, v, ref, scale, L, G, D):
+    """Per-element error bound of the kernel's fp32 arithmetic (see above)."""
+    kf = (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    vf = (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    tpb = 4 * (64 // (D // 8))                     # token slots per block
+    chunk = -(-(-(-L // 64)) // tpb) * tpb
+    dN = -(-chunk // tpb) + 8
+    dD = -(-chunk // 256) + 11
+    H = q.shape[0]
+    out = np.empty_like(ref)
+    for h in range(H):
+        g = h // G
+        absdot = np.abs(kf[:, g, :]) @ np.abs(q[h].astype(np.float64))
+        s = (kf[:, g, :] @ q[h].astype(np.float64)) * float(scale)
+        E = gamma(13) * float(scale) * absdot.max()
+        rho = 2 * E + U * np.max(s.max() - s) + 2.0 ** -22
+        vmax = np.abs(vf[:, g, :]).max()
+        out[h] = 2 * vmax * rho + gamma(dN) * vmax + gamma(dD) * np.abs(ref[h]) + ulp32(ref[h])
+    return out
+
+
+def check(env, L, H=20, Hkv=5, D=128, seed=0, kscale=1.0, data=None):
+    torch, tq, oracle = env
+    print(f"attn L={L} H={H} Hkv={Hkv} D={D}", flush=True)
+    q, k, v = make(L, H, Hkv, D, seed, kscale) if data is None else data
+    qt = torch.from_numpy(q).cuda()
+    kt = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda()
+    vt = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
+    out = tq.tq_attn_decode(qt, kt, vt)
+    torch.cuda.synchronize()
+    scale = np.float32(1.0 / np.sqrt(D))
+    ref = oracle.attn_decode(q, k, v, scale)
+    got = out.cpu().numpy().astype(np.float64)
+    tol = bound(q, k, v, ref, scale, L, H // Hkv, D)
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), float(np.max(err / tol))
+    return qt, kt, vt, out
+
+
+@pytest.mark.parametrize("L", [1, 7, 16, 100, 2048, 2049, 8192, 32768])
+def test_attn_2b4t_heads(env, L):
+    check(env, L, seed=L)
+
+
+@pytest.mark.parametrize("H,Hkv,D", [(8, 8, 128), (16, 8, 64), (32, 4, 128), (4, 1, 64)])
+def test_attn_group_sizes(env, H, Hkv, D):
+    check(env, 777, H, Hkv, D, seed=H + D)
+
+
+def test_attn_peaked_scores(env):
+    # large key scale: softmax concentrated on few tokens (max subtraction)
+    check(env, 4096, seed=5, kscale=30.0)
+
+
+def test_attn_exact_cases(env):
+    torch, tq, _ = env
+    # one token: weight exactly 1, so out is v (widened) bit for bit
+    q, k, v = make(1, 20, 5, 128, 21)
+    _, _, _, out = check(env, 1, data=(q, k, v))
+    vf = (v.astype(np.uint32) << 16).view(np.float32)
+    for h in range(20):
+        np.testing.assert_array_equal(out[h].cpu().numpy(), vf[0, h // 4])
+    # identical keys: every weight is exactly 1; out is the mean of v
+    q, k, v = make(300, 20, 5, 128, 22)
+    k[:] = k[0]
+    check(env, 300, data=(q, k, v))
+
+
+def test_attn_deterministic(env):
+    torch, tq, _ = env
+    qt, kt, vt, out = check(env, 5000, seed=6)
+    for _ in range(3):
+        again = tq.tq_attn_decode(qt, kt, vt)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int32), out.view(torch.int32))
