@@ -1,0 +1,105 @@
+"""Graph capture of the library calls that use scratch or several launches:
+tq_ternarize (a fill kernel clears its workspace, no memset node),
+tq_attn_decode (split + combine through a workspace) and the grouped
+quantize+GEMV.  Each graph is replayed several times with other eager work
+and synchronizations in between, and every replay must equal the eager
+result bit for bit.
+"""
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import bit_gemv_tq_amd as tq
+    return torch, tq
+
+
+def capture(torch, fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                                   # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_ternarize_graph(env):
+    torch, tq = env
+    print("graph: ternarize", flush=True)
+    bits = workloads.weights_bf16(256, 1024, seed=71)
+    w = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    ref_p, ref_s = tq.tq_ternarize(w)
+    torch.cuda.synchronize()
+    ref_p, ref_s = ref_p.clone(), ref_s.clone()
+    packed = torch.empty_like(ref_p)
+    scale = torch.empty_like(ref_s)
+    ws = torch.empty(tq.TQ_TERNARIZE_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    g = capture(torch, lambda: tq.tq_ternarize(w, packed, scale, ws))
+    for rep in range(4):
+        packed.fill_(0)
+        scale.fill_(0)
+        ws.fill_(0xFF)                         # stale workspace contents
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(packed, ref_p), rep
+        assert torch.equal(scale.view(torch.int32), ref_s.view(torch.int32)), rep
+
+
+def test_attn_graph(env):
+    torch, tq = env
+    print("graph: attention", flush=True)
+    torch.manual_seed(72)
+    q = torch.randn(20, 128, device="cuda")
+    k = torch.randn(3000, 5, 128, device="cuda").to(torch.bfloat16)
+    v = torch.randn(3000, 5, 128, device="cuda").to(torch.bfloat16)
+    ref = tq.tq_attn_decode(q, k, v)
+    torch.cuda.synchronize()
+    ref = ref.clone()
+    out = torch.empty_like(ref)
+    ws = torch.empty(tq.attn_workspace_bytes(20, 128), dtype=torch.uint8, device="cuda")
+    g = capture(torch, lambda: tq.tq_attn_decode(q, k, v, out=out, workspace=ws))
+    for rep in range(4):
+        out.fill_(7.0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), rep
+
+
+def test_group_graph(env):
+    torch, tq = env
+    print("graph: grouped quant_gemv", flush=True)
+    packs = []
+    for i, (N, K) in enumerate([(2560, 2560), (640, 2560), (640, 2560)]):
+        codes = workloads.ternary_codes(N, K, seed=73 + i)
+        packs.append(tq.tq_pack(torch.from_numpy(codes).cuda()))
+    xb = workloads.activations_bf16(1, 2560, seed=76, outliers=True)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()[0]
+    scales = [0.02, 0.021, 0.022]
+    ref = [t.clone() for t in tq.tq_quant_gemv_group(x, packs, scales)]
+    torch.cuda.synchronize()
+    ys = [torch.empty_like(t) for t in ref]
+    xq = torch.empty(2560, dtype=torch.int8, device="cuda")
+    xs = torch.empty(1, dtype=torch.float32, device="cuda")
+    g = capture(torch, lambda: tq.tq_quant_gemv_group(x, packs, scales, ys, xq=xq, x_scale=xs))
+    for rep in range(4):
+        for t in ys:
+            t.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ys, ref):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
