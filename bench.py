@@ -581,7 +581,7 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
     H, Hkv, D = 20, 5, 128
     qa = torch.randn(H, D, device=dev, dtype=torch.float32)
     oa = torch.empty(H, D, device=dev, dtype=torch.float32)
-    wsa = torch.empty(tq.attn_workspace_bytes(H, D), dtype=torch.uint8, device=dev)
+    wsa = tq.attn_workspace(H, D, 32768, dev)
     for L in (2048, 8192, 32768):
         kv_bytes = 2 * L * Hkv * D * 2
         copies = max(4, -(-(640 << 20) // kv_bytes))

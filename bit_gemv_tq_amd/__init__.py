@@ -59,7 +59,7 @@ def _load() -> ctypes.CDLL:
         # host arrays: packed**, w_scale*, N*, y**, acc** (ctypes arrays)
         "tq_quant_gemv_group": [p, i32, i32, p, p, p, i64, p, p, p, p, p, p],
         "tq_ternarize": [p, i64, i64, p, p, p, p],
-        "tq_attn_decode": [p, p, p, i64, i64, i64, i64, f32, p, p, p],
+        "tq_attn_decode": [p, p, p, i64, i64, i64, i64, f32, p, p, ctypes.c_size_t, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -338,15 +338,30 @@ def tq_ternarize(w, packed=None, w_scale=None, workspace=None, stream=None):
     return packed, w_scale
 
 
-def attn_workspace_bytes(H: int, D: int) -> int:
-    return H * 64 * (D + 2) * 8
+TQ_ATTN_MAX_L = 131072
+
+
+def attn_workspace_bytes(H: int, D: int, L: int) -> int:
+    """TQ_ATTN_WORKSPACE_BYTES(H, D, L): per-chunk partial results."""
+    return H * ((L + 63) // 64) * (D + 4) * 4
+
+
+_attn_ws_cache = {}
+
+
+def attn_workspace(H: int, D: int, L: int, device):
+    """A workspace for tq_attn_decode calls with these H, D and any length up to L."""
+    torch = _torch()
+    return torch.empty(attn_workspace_bytes(H, D, L), dtype=torch.uint8, device=device)
 
 
 def tq_attn_decode(q, k_cache, v_cache, scale=None, out=None, workspace=None,
                    stream=None):
     """Attention of one query token: q fp32 [H, D], k/v bf16 [L, Hkv, D] ->
-    out fp32 [H, D] (fp64 inside, one rounding).  scale defaults to
-    1/sqrt(D) rounded to fp32.  The workspace is allocated when not given."""
+    out fp32 [H, D] (fp32 within chunks, fp64 merge, one rounding).  scale
+    defaults to 1/sqrt(D) rounded to fp32.  Without a workspace, one per
+    device is kept and grown as needed (calls that may overlap on different
+    streams must pass their own)."""
     torch = _torch()
     _need(q, "q", torch.float32)
     dev = q.device
@@ -361,14 +376,19 @@ def tq_attn_decode(q, k_cache, v_cache, scale=None, out=None, workspace=None,
     if scale is None:
         scale = ctypes.c_float(1.0 / math.sqrt(D)).value
     out = _out(out, "out", (H, D), torch.float32, dev)
-    need = attn_workspace_bytes(H, D)
+    need = attn_workspace_bytes(H, D, L)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        key = (dev.type, dev.index)
+        workspace = _attn_ws_cache.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = attn_workspace(H, D, L, dev)
+            _attn_ws_cache[key] = workspace
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace too small")
     _check("tq_attn_decode", lib.tq_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), H, Hkv, D, L, float(scale),
-        _ptr(out), _ptr(workspace), _stream(stream)))
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return out
 
 

@@ -8,19 +8,27 @@
 // precision; this library computes
 //   s[h,t] = scale * sum_d q[h,d] k[t,g,d],  g = h / (H/Hkv)
 //   o[h,:] = sum_t softmax_t(s[h,:]) v[t,g,:]
-// in fp32 (bf16 inputs widen exactly; fp32 FMAs, expf) within each split,
-// and merges the splits in fp64.  Every summation order is fixed (no
+// in fp32 (bf16 inputs widen exactly; fp32 FMAs, expf) within each chunk of
+// tokens, and merges the chunks in fp64.  Every summation order is fixed (no
 // atomics), so identical calls give identical bits.  The op streams the KV
 // cache once: HBM bound at long contexts.
 //
-// Split pass: block (g, c) handles the G query heads of KV head g over the
-// token chunk c.  A token row of one KV head (D bf16 = 2D bytes) is read by
+// Chunk pass: block (g, c) handles the G query heads of KV head g over the
+// tokens of chunk c (at most kAttnMaxSplits chunks per KV head), in steps of
+// STEP tokens.  A token row of one KV head (D bf16 = 2D bytes) is read by
 // LPT = D/8 consecutive lanes, 16 bytes each; a lane slot takes kT tokens per
-// step, so each lane has kT row loads in flight.  The kT*G partial dots of a
+// step, and the next step's rows are loaded during this step's arithmetic.  The kT*G partial dots of a
 // slot are summed by a reduce-scatter butterfly over its LPT lanes.  Scores,
-// then weights, live in LDS; the chunk's max, exp-sum and unnormalized
-// output per head go to the workspace.  Combine pass: one block per query
-// head merges the chunks in order.
+// then weights, live in LDS; the first step's V rows are loaded while the
+// softmax statistics are formed.  The chunk's max m, exp-sum l and
+// unnormalized output o go to the workspace (fp32: they are fp32 sums).  A
+// single chunk writes the output itself.
+//
+// Combine pass: block (h, slice) merges the chunks of query head h for 32
+// dims in fp64, all of its loads issued at once (one memory round trip).
+// A second launch, not a last-arriving block: a device-wide handoff inside
+// one launch costs a store acknowledgement, an atomic and a load, about
+// three memory round trips on this chip, against one launch gap here.
 #include <math.h>
 
 #include "tq_device.h"
@@ -30,13 +38,53 @@ namespace tq {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kAttnMaxSplits = 64;
-constexpr int kAttnMaxChunk = 2048;
+constexpr int kAttnNW = kAttnThreads / kWave;
+constexpr int kAttnMinChunk = 64;    // smallest step of any (G, D, kT)
+constexpr int kAttnMaxSplits = 64;   // chunks per KV head
+constexpr int kCombineDims = 32;     // dims per combine block
+constexpr int kCombineSubs = kAttnThreads / kCombineDims;  // row subranges
+constexpr int kCombineBatch = kAttnMaxSplits / kCombineSubs;  // rows per thread
 
-// Workspace layout (fp64): for split c of head h: m, l, then D values of o.
-__host__ __device__ inline size_t ws_index(int h, int c, int D) {
-  return ((size_t)h * kAttnMaxSplits + c) * (size_t)(D + 2);
+// Per (G, D, kT): lanes per token row, token slots, tokens per block step.
+// kT (tokens per lane slot and step) is at least LPT/G so that every lane
+// ends the butterfly with a complete sum.
+template <int G, int D, int KT>
+struct AttnShape {
+  static constexpr int LPT = D / 8;          // lanes per token row
+  static constexpr int TPW = kWave / LPT;    // token slots per wave
+  static constexpr int TPB = kAttnNW * TPW;  // token slots per block
+  static constexpr int kT = KT;
+  static constexpr int CH = TPB * kT;         // tokens per block step
+  static constexpr int NV = kT * G;           // partial dots per lane
+  static constexpr int VPL = NV / LPT;        // complete sums per lane
+  static constexpr bool kPrefetchV = kT <= 8;  // V rows loaded with K rows
+  static_assert(NV % LPT == 0 && VPL >= 1, "butterfly shape");
+  static_assert(CH >= kAttnMinChunk, "workspace sized for 64-token steps");
+};
+// Long contexts: kT = max(LPT/G, min(8, 32/G)) (at most 32 partial dots per
+// lane); short ones: at most 4 (smaller steps, so more chunks and less
+// serial work per block).
+template <int G, int D>
+constexpr int kt_long() {
+  return D / 8 / G > (32 / G < 8 ? 32 / G : 8) ? D / 8 / G : (32 / G < 8 ? 32 / G : 8);
 }
+template <int G, int D>
+constexpr int kt_short() {
+  return D / 8 / G > (kt_long<G, D>() < 4 ? kt_long<G, D>() : 4)
+             ? D / 8 / G
+             : (kt_long<G, D>() < 4 ? kt_long<G, D>() : 4);
+}
+
+struct AttnArgs {
+  const float *q;         // [H, D]
+  const uint16_t *k, *v;  // [L, Hkv, D] bf16
+  int Hkv, L;
+  int chunk;              // tokens per chunk (whole steps)
+  int S;                  // chunks per KV head
+  float scale;
+  float *part;            // [H][S][D + 4]: o[D], m, l, 2 unused
+  float *out;             // [H, D]
+};
 
 __device__ __forceinline__ void widen8(const u32x4 &r, float (&x)[8]) {
 #pragma unroll
@@ -64,59 +112,57 @@ __device__ __forceinline__ void reduce_scatter(float (&val)[N], int lt) {
   }
 }
 
-template <int G, int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
-    const float *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, int Hkv, int L, int chunk, float scale,
-    double *__restrict__ ws) {
-  constexpr int LPT = D / 8;             // lanes per token row
-  constexpr int TPW = kWave / LPT;       // token slots per wave
-  constexpr int NW = kAttnThreads / kWave;
-  constexpr int TPB = NW * TPW;          // token slots per block
-  // kT tokens per slot per step: at least LPT/G (every lane ends with a
-  // complete sum), 8 otherwise, at most 32/G partial dots (registers).
-  constexpr int kTcap = 32 / G < 8 ? 32 / G : 8;
-  constexpr int kT = LPT / G > kTcap ? LPT / G : kTcap;
-  constexpr int NV = kT * G;             // partial dots per lane
-  constexpr int VPL = NV / LPT;          // complete sums per lane at the end
-  static_assert(NV % LPT == 0 && VPL >= 1, "butterfly shape");
-  // Dynamic LDS: [G][chunk] scores, then weights; after the P.V loop the
-  // same space holds the per-wave outputs [NW][G][D].
+template <int G, int D, int KT>
+__global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
+  using Sh = AttnShape<G, D, KT>;
+  constexpr int LPT = Sh::LPT, TPW = Sh::TPW, kT = Sh::kT, STEP = Sh::CH;
+  constexpr int NV = Sh::NV, VPL = Sh::VPL, NW = kAttnNW;
+  // Dynamic LDS: scores [G][chunk], then weights; after the P.V loop the
+  // per-wave outputs [NW][G][D].
   extern __shared__ float s_lds[];
   __shared__ float red[NW][G];
 
+  const int chunk = a.chunk;
   const int g = blockIdx.x, c = blockIdx.y;
-  const int t0 = c * chunk, t1 = min(t0 + chunk, L);
-  const int n = t1 - t0;
+  const int t0 = c * chunk;
+  const int n = min(chunk, a.L - t0);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int lt = lane % LPT;            // piece of the row (8 dims)
-  const int tw = lane / LPT;            // token slot within the wave
+  const int lt = lane % LPT;       // piece of the row (8 dims)
+  const int tw = lane / LPT;       // token slot within the wave
+  const int i0 = wave * TPW * kT;  // this wave's first token of a step
+
+  // token of slot step u in the step starting at `it` (wave-uniform `it`)
+  auto row = [&](const uint16_t *base, int i) {
+    const int t = t0 + (i < n ? i : 0);  // past the chunk: an in-chunk row
+    return *reinterpret_cast<const u32x4 *>(base + ((size_t)t * a.Hkv + g) * D + lt * 8);
+  };
 
   float qd[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const float4 *qp = reinterpret_cast<const float4 *>(q + (size_t)(g * G + j) * D + lt * 8);
-    const float4 a = qp[0], b = qp[1];
-    qd[j][0] = a.x; qd[j][1] = a.y; qd[j][2] = a.z; qd[j][3] = a.w;
-    qd[j][4] = b.x; qd[j][5] = b.y; qd[j][6] = b.z; qd[j][7] = b.w;
+    const float4 *qp = reinterpret_cast<const float4 *>(a.q + (size_t)(g * G + j) * D + lt * 8);
+    const float4 x0 = qp[0], x1 = qp[1];
+    qd[j][0] = x0.x; qd[j][1] = x0.y; qd[j][2] = x0.z; qd[j][3] = x0.w;
+    qd[j][4] = x1.x; qd[j][5] = x1.y; qd[j][6] = x1.z; qd[j][7] = x1.w;
   }
-  auto row = [&](const uint16_t *base, int t) {
-    return *reinterpret_cast<const u32x4 *>(base + ((size_t)t * Hkv + g) * D + lt * 8);
-  };
 
-  // 1. scores: token i = it + u*TPW + tw for u < kT (it advancing by TPB*kT)
-  for (int it = wave * TPW * kT; it < n; it += TPB * kT) {
-    u32x4 r[kT];
+  // 1. scores, one step at a time, the next step's K rows in flight during
+  // this step's arithmetic: after the reduce-scatter lane lt holds the
+  // complete sums of values v = VPL*lt + b (v = u*G + j)
+  // (Loads are unconditional, past the chunk they re-read an in-chunk row,
+  // so the compiler's wait counts cover exactly the rows a step needs.)
+  u32x4 rk[kT];
 #pragma unroll
-    for (int u = 0; u < kT; ++u) {
-      const int i = it + u * TPW + tw;
-      r[u] = row(kc, t0 + (i < n ? i : 0));  // past the chunk: an in-chunk row
-    }
+  for (int u = 0; u < kT; ++u) rk[u] = row(a.k, i0 + u * TPW + tw);
+  for (int it = i0; it < n; it += STEP) {
+    u32x4 rkn[kT];
+#pragma unroll
+    for (int u = 0; u < kT; ++u) rkn[u] = row(a.k, it + STEP + u * TPW + tw);
     float val[NV];
 #pragma unroll
     for (int u = 0; u < kT; ++u) {
       float x[8];
-      widen8(r[u], x);
+      widen8(rk[u], x);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float dsum = 0.0f;
@@ -125,18 +171,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
         val[u * G + j] = dsum;
       }
     }
-    // reduce-scatter: after the step with offset `off` a lane keeps the half
-    // of its values selected by its bit `off`; lane lt ends with the complete
-    // sums of values v = VPL*lt + b (v = u*G + j)
     reduce_scatter<LPT / 2, NV>(val, lt);
 #pragma unroll
     for (int b = 0; b < VPL; ++b) {
       const int v = VPL * lt + b;
-      const int u = v / G, j = v % G;
-      const int i = it + u * TPW + tw;
-      if (i < n) s_lds[j * chunk + i] = val[b] * scale;
+      const int i = it + (v / G) * TPW + tw;
+      if (i < n) s_lds[(v % G) * chunk + i] = val[b] * a.scale;
     }
+#pragma unroll
+    for (int u = 0; u < kT; ++u) rk[u] = rkn[u];
   }
+  // the first P.V step's V rows, in flight during the softmax statistics
+  u32x4 rv[kT];
+#pragma unroll
+  for (int u = 0; u < kT; ++u) rv[u] = row(a.v, i0 + u * TPW + tw);
   __syncthreads();
 
   // 2. per-head max and exp-sum over the chunk (fixed reduction order)
@@ -175,33 +223,43 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
     for (int w = 1; w < NW; ++w) sum[j] += red[w][j];
   }
 
-  // 3. unnormalized output sum_t p[t] v[t] over the chunk, kT rows in flight
+  // 3. unnormalized output sum_t p[t] v[t] over the chunk
   float acc[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
-  for (int it = wave * TPW * kT; it < n; it += TPB * kT) {
-    u32x4 r[kT];
+  auto pv_step = [&](const u32x4 (&r)[kT], int it) {
 #pragma unroll
     for (int u = 0; u < kT; ++u) {
+      // past the chunk: weight 0 on a re-read in-chunk row (adds +-0 exactly;
+      // no branch, so the next step's loads stay in flight)
       const int i = it + u * TPW + tw;
-      r[u] = row(vc, t0 + (i < n ? i : 0));
-    }
+      const int ic = i < n ? i : n - 1;
+      const float keep = i < n ? 1.0f : 0.0f;
+      float x[8];
+      widen8(r[u], x);
 #pragma unroll
-    for (int u = 0; u < kT; ++u) {
-      const int i = it + u * TPW + tw;
-      if (i < n) {
-        float x[8];
-        widen8(r[u], x);
+      for (int j = 0; j < G; ++j) {
+        const float p = s_lds[j * chunk + ic] * keep;
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float p = s_lds[j * chunk + i];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, x[e], acc[j][e]);
-        }
+        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, x[e], acc[j][e]);
       }
     }
+  };
+  auto load_v = [&](u32x4 (&r)[kT], int it) {
+#pragma unroll
+    for (int u = 0; u < kT; ++u) r[u] = row(a.v, it + u * TPW + tw);
+  };
+  // two steps per trip through two register sets (no copies between them,
+  // so one set's loads stay in flight while the other is consumed)
+  for (int it = i0; it < n; it += 2 * STEP) {
+    u32x4 rv2[kT];
+    load_v(rv2, it + STEP);
+    pv_step(rv, it);
+    if (it + STEP >= n) break;  // wave-uniform
+    load_v(rv, it + 2 * STEP);
+    pv_step(rv2, it + STEP);
   }
   // token slots of a wave (lanes LPT apart), then the waves, in order
 #pragma unroll
@@ -219,107 +277,139 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
       for (int e = 0; e < 8; ++e) o_red[(wave * G + j) * D + lt * 8 + e] = acc[j][e];
   }
   __syncthreads();
+
+  // 5. this chunk's result: the output itself when it is the only chunk,
+  // else a partial row
+  constexpr int RS = D + 4;  // partial row stride (floats)
   for (int idx = threadIdx.x; idx < G * D; idx += kAttnThreads) {
     const int j = idx / D, d = idx % D;
     float o = o_red[j * D + d];
 #pragma unroll
     for (int w = 1; w < NW; ++w) o += o_red[(w * G + j) * D + d];
-    ws[ws_index(g * G + j, c, D) + 2 + d] = (double)o;
+    const size_t h = (size_t)(g * G + j);
+    if (a.S == 1)
+      a.out[h * D + d] = (float)((double)o / (double)sum[j]);
+    else
+      a.part[(h * a.S + c) * RS + d] = o;
   }
-  if (threadIdx.x < G) {
+  if (a.S > 1 && threadIdx.x < G) {
     const int j = threadIdx.x;
-    ws[ws_index(g * G + j, c, D)] = (double)mx[j];
-    ws[ws_index(g * G + j, c, D) + 1] = (double)sum[j];
+    float *p = a.part + ((size_t)(g * G + j) * a.S + c) * RS + D;
+    p[0] = mx[j];
+    p[1] = sum[j];
   }
 }
 
-// One block per query head: merge the splits in order, round once.  The
-// per-split maxima and weights are loaded in parallel and staged in LDS; the
-// output sums keep 8 loads in flight per thread.
-constexpr int kCombineThreads = 128;
-
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
-    const double *__restrict__ ws, int splits, int D, float *__restrict__ out) {
-  __shared__ double f[kAttnMaxSplits];   // exp(m_c - M)
-  __shared__ double ls[kAttnMaxSplits];  // l_c
-  __shared__ double wmax[kCombineThreads / kWave];
+// Block (h, slice): out[h, d] for kCombineDims dims d, merging the S <=
+// kAttnMaxSplits (one wave's width) chunk results of head h in fp64, all
+// loads issued at once:
+//   M = max_c m_c,  den = sum_c e^(m_c - M) l_c,  out = sum_c e^(m_c - M) o_c / den
+// M and den: lane c of wave 0 holds chunk c, fixed butterfly trees (the
+// value of lane 0 is used).  Thread (sub, dd) sums the chunks c = sub,
+// sub + kCombineSubs, ... in order; the subranges are added in order.
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
+    const float *__restrict__ part, int S, int D, float *__restrict__ out) {
+  static_assert(kAttnMaxSplits == kWave, "one chunk per lane of wave 0");
+  __shared__ double f[kAttnMaxSplits];  // e^(m_c - M)
   __shared__ double den_s;
+  __shared__ double num_s[kCombineSubs][kCombineDims];
   const int h = blockIdx.x;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int c = threadIdx.x;
-  const double m = c < splits ? ws[ws_index(h, c, D)] : -INFINITY;
-  const double l = c < splits ? ws[ws_index(h, c, D) + 1] : 0.0;
-  double M = m;
-  for (int off = kWave / 2; off >= 1; off >>= 1) M = fmax(M, __shfl_xor(M, off, kWave));
-  if (lane == 0) wmax[wave] = M;
-  __syncthreads();
-  M = wmax[0];
+  const int dd = threadIdx.x % kCombineDims, sub = threadIdx.x / kCombineDims;
+  const int d = blockIdx.y * kCombineDims + dd;
+  const int RS = D + 4;
+  const float *ph = part + (size_t)h * S * RS;
+  const int tid = threadIdx.x;
+
+  float mv = -INFINITY, lv = 0.0f;
+  if (tid < S) {
+    mv = ph[(size_t)tid * RS + D];
+    lv = ph[(size_t)tid * RS + D + 1];
+  }
+  float ov[kCombineBatch];
 #pragma unroll
-  for (int w = 1; w < kCombineThreads / kWave; ++w) M = fmax(M, wmax[w]);
-  if (c < kAttnMaxSplits) {  // splits past the end weigh exactly 0
-    f[c] = c < splits ? exp(m - M) : 0.0;
-    ls[c] = l;
+  for (int u = 0; u < kCombineBatch; ++u) {  // past the end: weight 0
+    const int c = sub + u * kCombineSubs;
+    ov[u] = c < S ? ph[(size_t)c * RS + d] : 0.0f;
+  }
+  if (tid < kWave) {
+    double M = (double)mv;
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) M = fmax(M, __shfl_xor(M, off, kWave));
+    const double e = tid < S ? exp((double)mv - M) : 0.0;
+    f[tid] = e;
+    double den = e * (double)lv;
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
+    if (tid == 0) den_s = den;
   }
   __syncthreads();
-  if (c == 0) {  // fixed order
-    double den = 0.0;
-    for (int i = 0; i < splits; ++i) den = fma(f[i], ls[i], den);
-    den_s = den;
+  double num = 0.0;
+#pragma unroll
+  for (int u = 0; u < kCombineBatch; ++u) {
+    const int c = sub + u * kCombineSubs;
+    num = fma(c < S ? f[c] : 0.0, (double)ov[u], num);
   }
+  num_s[sub][dd] = num;
   __syncthreads();
-  const double den = den_s;
-  for (int d = threadIdx.x; d < D; d += kCombineThreads) {
-    // splits summed in order, kUnroll loads issued per round
-    constexpr int kUnroll = 8;  // loads in flight per thread
-    double num = 0.0;
-    for (int i0 = 0; i0 < splits; i0 += kUnroll) {
-      double o[kUnroll];
+  if (sub == 0) {
+    double t = num_s[0][dd];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)  // past the end: weight 0, valid row
-        o[u] = ws[ws_index(h, min(i0 + u, splits - 1), D) + 2 + d];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        num = fma(i0 + u < kAttnMaxSplits ? f[i0 + u] : 0.0, o[u], num);
-    }
-    out[(size_t)h * D + d] = (float)(num / den);
+    for (int q = 1; q < kCombineSubs; ++q) t += num_s[q][dd];
+    out[(size_t)h * D + d] = (float)(t / den_s);
   }
 }
+
+template <int G, int D, int KT>
+tq_status launch_attn(const float *q, const void *k, const void *v, int H,
+                      int Hkv, int L, float scale, float *out, float *part,
+                      hipStream_t s) {
+  // At most kAttnMaxSplits chunks per KV head, each a whole number of steps.
+  constexpr int STEP = AttnShape<G, D, KT>::CH;
+  const int steps = (L + STEP * kAttnMaxSplits - 1) / (STEP * kAttnMaxSplits);
+  AttnArgs a;
+  a.q = q;
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.Hkv = Hkv;
+  a.L = L;
+  a.chunk = steps * STEP;
+  a.S = (L + a.chunk - 1) / a.chunk;
+  a.scale = scale;
+  a.part = part;
+  a.out = out;
+  constexpr int kOutFloats = kAttnNW * G * D;
+  const size_t lds = (size_t)(G * a.chunk > kOutFloats ? G * a.chunk : kOutFloats) * 4;
+  if (tq_status st = allow_dynamic_lds((const void *)attn_chunk_kernel<G, D, KT>, (int)lds))
+    return st;
+  if (tq_status st = launch(attn_chunk_kernel<G, D, KT>, dim3(Hkv, a.S),
+                            dim3(kAttnThreads), lds, s, a))
+    return st;
+  if (a.S == 1) return TQ_OK;
+  return launch(attn_combine_kernel, dim3(H, D / kCombineDims), dim3(kAttnThreads), 0, s,
+                static_cast<const float *>(part), a.S, D, out);
+}
+
+// Chunk size by context length: short contexts take the small chunks.
+constexpr int kAttnShortL = 8192;
 
 template <int G, int D>
-tq_status launch_attn(const float *q, const void *k, const void *v, int H,
-                      int Hkv, int L, float scale, float *out, double *ws,
-                      hipStream_t s) {
-  // Chunks: about kAttnMaxSplits per KV head (enough blocks to spread the
-  // cache over every CU), a multiple of the tokens a block steps by.
-  constexpr int TPB = (kAttnThreads / kWave) * (kWave / (D / 8));
-  int chunk = (L + kAttnMaxSplits - 1) / kAttnMaxSplits;
-  chunk = (chunk + TPB - 1) / TPB * TPB;  // whole block steps
-  if (chunk > kAttnMaxChunk) return TQ_ERR_SHAPE;  // excluded by the caller
-  const int splits = (L + chunk - 1) / chunk;
-  constexpr int kOutFloats = (kAttnThreads / kWave) * G * D;
-  const size_t lds = (size_t)(G * chunk > kOutFloats ? G * chunk : kOutFloats) *
-                     sizeof(float);
-  if (tq_status st = allow_dynamic_lds((const void *)attn_split_kernel<G, D>, (int)lds))
-    return st;
-  if (tq_status st = launch(attn_split_kernel<G, D>, dim3(Hkv, splits),
-                            dim3(kAttnThreads), lds, s, q,
-                            static_cast<const uint16_t *>(k),
-                            static_cast<const uint16_t *>(v), Hkv, L, chunk,
-                            scale, ws))
-    return st;
-  return launch(attn_combine_kernel, dim3(H), dim3(kCombineThreads), 0, s,
-                static_cast<const double *>(ws), splits, D, out);
+tq_status launch_attn_g(const float *q, const void *k, const void *v, int H,
+                        int Hkv, int L, float scale, float *out, float *part,
+                        hipStream_t s) {
+  if (L <= kAttnShortL)
+    return launch_attn<G, D, kt_short<G, D>()>(q, k, v, H, Hkv, L, scale, out, part, s);
+  return launch_attn<G, D, kt_long<G, D>()>(q, k, v, H, Hkv, L, scale, out, part, s);
 }
 
 template <int D>
 tq_status launch_attn_d(int G, const float *q, const void *k, const void *v,
                         int H, int Hkv, int L, float scale, float *out,
-                        double *ws, hipStream_t s) {
+                        float *part, hipStream_t s) {
   switch (G) {
-    case 1: return launch_attn<1, D>(q, k, v, H, Hkv, L, scale, out, ws, s);
-    case 2: return launch_attn<2, D>(q, k, v, H, Hkv, L, scale, out, ws, s);
-    case 4: return launch_attn<4, D>(q, k, v, H, Hkv, L, scale, out, ws, s);
-    case 8: return launch_attn<8, D>(q, k, v, H, Hkv, L, scale, out, ws, s);
+    case 1: return launch_attn_g<1, D>(q, k, v, H, Hkv, L, scale, out, part, s);
+    case 2: return launch_attn_g<2, D>(q, k, v, H, Hkv, L, scale, out, part, s);
+    case 4: return launch_attn_g<4, D>(q, k, v, H, Hkv, L, scale, out, part, s);
+    case 8: return launch_attn_g<8, D>(q, k, v, H, Hkv, L, scale, out, part, s);
   }
   return TQ_ERR_SHAPE;
 }
@@ -331,22 +421,23 @@ extern "C" tq_status tq_attn_decode(const float *q, const void *k_cache,
                                     const void *v_cache, int64_t H, int64_t Hkv,
                                     int64_t D, int64_t L, float scale,
                                     float *out, void *workspace,
-                                    hipStream_t stream) {
+                                    size_t workspace_bytes, hipStream_t stream) {
   using namespace tq;
   if (H < 1 || Hkv < 1 || H % Hkv != 0 || H > 256) return TQ_ERR_SHAPE;
   const int64_t G = H / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_ERR_SHAPE;
   if (D != 64 && D != 128) return TQ_ERR_SHAPE;
-  if (L < 1 || L > (int64_t)kAttnMaxSplits * kAttnMaxChunk) return TQ_ERR_SHAPE;
+  if (L < 1 || L > TQ_ATTN_MAX_L) return TQ_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !out || !workspace) return TQ_ERR_NULL;
+  if (workspace_bytes < TQ_ATTN_WORKSPACE_BYTES(H, D, L)) return TQ_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(out, 4) || !aligned(workspace, 8))
+      !aligned(out, 4) || !aligned(workspace, 16))
     return TQ_ERR_ALIGN;
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
-  auto *ws = static_cast<double *>(workspace);
+  auto *part = static_cast<float *>(workspace);
   return D == 128 ? launch_attn_d<128>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
-                                       (int)L, scale, out, ws, stream)
+                                       (int)L, scale, out, part, stream)
                   : launch_attn_d<64>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
-                                      (int)L, scale, out, ws, stream);
+                                      (int)L, scale, out, part, stream);
 }

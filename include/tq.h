@@ -245,22 +245,29 @@ TQ_API tq_status tq_ternarize(const void *w, int64_t N, int64_t K,
  * 5 KV heads, head_dim 128).  The pages give no formula; this library's:
  *   s[h,t] = scale * sum_d q[h,d] k[t,g,d],   g = h / (H/Hkv)
  *   out[h,:] = sum_t softmax_t(s[h,:]) v[t,g,:]
- * evaluated in fp64 (exact widening of the inputs) and rounded once to fp32;
- * the summation order is fixed, so identical calls give identical bits.
+ * Scores, weights and the sums over a chunk of tokens are fp32 (the bf16
+ * inputs widen exactly); the chunks are merged in fp64 and the result is
+ * rounded once to fp32.  Summation orders are fixed, so identical calls give
+ * identical bits.
  *   q          fp32 [H, D] device, 16-B aligned.
  *   k_cache, v_cache  bf16 [L, Hkv, D] device (token-major), 16-B aligned.
  *   out        fp32 [H, D] device output.
- *   workspace  device scratch of TQ_ATTN_WORKSPACE_BYTES(H, D) bytes, 8-B
- *              aligned, any contents (per-split partial results); calls that
- *              overlap in time must not share one workspace.
- * H % Hkv == 0 with H/Hkv in {1, 2, 4, 8}; D in {64, 128}; 1 <= L <= 131072.
- * Two launches (split pass, combine).
+ *   workspace  device memory of workspace_bytes >=
+ *              TQ_ATTN_WORKSPACE_BYTES(H, D, L) bytes, 16-B aligned, any
+ *              contents (per-chunk partial results).  Calls that overlap in
+ *              time must not share one workspace.
+ * H % Hkv == 0 with H/Hkv in {1, 2, 4, 8}; D in {64, 128};
+ * 1 <= L <= TQ_ATTN_MAX_L; a workspace below the size is TQ_ERR_SHAPE.  Two
+ * launches (chunk pass, combine); one when L fits in one chunk.
  */
-#define TQ_ATTN_WORKSPACE_BYTES(H, D) ((size_t)(H) * 64u * ((size_t)(D) + 2u) * 8u)
+#define TQ_ATTN_MAX_L 131072
+#define TQ_ATTN_WORKSPACE_BYTES(H, D, L) \
+  ((size_t)(H) * (((size_t)(L) + 63u) / 64u) * ((size_t)(D) + 4u) * 4u)
 TQ_API tq_status tq_attn_decode(const float *q, const void *k_cache,
                                 const void *v_cache, int64_t H, int64_t Hkv,
                                 int64_t D, int64_t L, float scale, float *out,
-                                void *workspace, hipStream_t stream);
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 TQ_API const char *tq_status_string(tq_status status);

@@ -176,18 +176,29 @@ def test_ternarize_validation(tq):
 
 def test_attn_decode_validation(tq):
     f = tq.lib.tq_attn_decode
-    #        q  k  v   H  Hkv  D    L   scale  out ws  stream
-    assert f(A, A, A, 20, 3, 128, 16, 0.1, A, A, None) == SHAPE      # H % Hkv
-    assert f(A, A, A, 48, 4, 128, 16, 0.1, A, A, None) == SHAPE      # group 12
-    assert f(A, A, A, 20, 5, 96, 16, 0.1, A, A, None) == SHAPE       # D
-    assert f(A, A, A, 20, 5, 128, 0, 0.1, A, A, None) == SHAPE       # L = 0
-    assert f(A, A, A, 20, 5, 128, 131073, 0.1, A, A, None) == SHAPE
-    assert f(None, A, A, 20, 5, 128, 16, 0.1, A, A, None) == NULL
-    assert f(A, A, A, 20, 5, 128, 16, 0.1, A, None, None) == NULL
-    assert f(MIS, A, A, 20, 5, 128, 16, 0.1, A, A, None) == ALIGN
-    assert f(A, MIS, A, 20, 5, 128, 16, 0.1, A, A, None) == ALIGN
-    assert f(A, A, A, 20, 5, 128, 16, 0.1, ODD, A, None) == ALIGN
-    assert f(A, A, A, 20, 5, 128, 16, 0.1, A, P(0x10004), None) == ALIGN
+    W = tq.attn_workspace_bytes(20, 128, 16)
+    #        q  k  v   H  Hkv  D    L   scale  out ws  bytes stream
+    assert f(A, A, A, 20, 3, 128, 16, 0.1, A, A, W, None) == SHAPE      # H % Hkv
+    assert f(A, A, A, 48, 4, 128, 16, 0.1, A, A, W, None) == SHAPE      # group 12
+    assert f(A, A, A, 20, 5, 96, 16, 0.1, A, A, W, None) == SHAPE       # D
+    assert f(A, A, A, 20, 5, 128, 0, 0.1, A, A, W, None) == SHAPE       # L = 0
+    assert f(A, A, A, 20, 5, 128, 131073, 0.1, A, A, 1 << 40, None) == SHAPE
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, A, A, W - 1, None) == SHAPE  # workspace
+    assert f(A, A, A, 20, 5, 128, 64 * 1000 + 1, 0.1, A, A,
+             tq.attn_workspace_bytes(20, 128, 64 * 1000), None) == SHAPE
+    assert f(None, A, A, 20, 5, 128, 16, 0.1, A, A, W, None) == NULL
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, A, None, W, None) == NULL
+    assert f(MIS, A, A, 20, 5, 128, 16, 0.1, A, A, W, None) == ALIGN
+    assert f(A, MIS, A, 20, 5, 128, 16, 0.1, A, A, W, None) == ALIGN
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, ODD, A, W, None) == ALIGN
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, A, P(0x10008), W, None) == ALIGN
+
+
+def test_attn_workspace_size(tq):
+    # TQ_ATTN_WORKSPACE_BYTES: H x ceil(L / 64) fp32 chunk rows of D + 4
+    assert tq.attn_workspace_bytes(20, 128, 2048) == 20 * 32 * 132 * 4
+    assert tq.attn_workspace_bytes(1, 64, 1) == 68 * 4
+    assert tq.attn_workspace_bytes(20, 128, 2049) == 20 * 33 * 132 * 4
 
 
 def test_pack_validation(tq):
@@ -214,7 +225,8 @@ def test_no_device_is_reported(tq):
     assert tq.lib.tq_act_quant(A, 0, 1, 64, A, A, None) == DEVICE
     assert tq.lib.tq_pack(A, 8, 16, A, None) == DEVICE
     assert tq.lib.tq_ternarize(A, 8, 16, A, A, A, None) == DEVICE
-    assert tq.lib.tq_attn_decode(A, A, A, 20, 5, 128, 16, 0.1, A, A, None) == DEVICE
+    assert tq.lib.tq_attn_decode(A, A, A, 20, 5, 128, 16, 0.1, A, A,
+                                 tq.attn_workspace_bytes(20, 128, 16), None) == DEVICE
     assert tq.lib.tq_gemm_small(A, 0.02, A, A, 4, 64, 64, A, None, None) == DEVICE
     assert tq.lib.tq_quant_gemv(A, 0, A, 0.02, 64, 64, A, None, A, A, None,
                                 None) == DEVICE

@@ -4,6 +4,11 @@ head layout (20 query heads, 5 KV heads, D = 128) for L from 1 to 32768
 softmax, exact cases (one token: out == v; identical keys), and bitwise
 determinism across calls.
 
+Covered: one chunk (the chunk pass writes the output), the combine over 2
+to 64 chunks of one or several steps, both step sizes (contexts up to 8192
+take the smaller), ragged last steps and chunks, and one workspace reused
+across calls of different lengths.
+
 Tolerance (derived from the kernel's fp32 arithmetic, per head h):
   E   = gamma(13) * scale * max_t sum_d |q[h,d] k[t,d]|   (score error: an
         8-term FMA chain, a 16-lane tree, the scale product)
@@ -49,13 +54,25 @@ def gamma(n):
     return n * U / (1 - n * U)
 
 
+def chunk_shape(G, D, L):
+    """Tokens per lane slot over a chunk, and tokens per chunk, of the
+    kernel's layout: per step at most 8 per slot (4 up to L = 8192), at
+    least D/8/G; whole steps per chunk, at most 64 chunks."""
+    lpt = D // 8                                   # lanes per token row
+    tpb = 4 * (64 // lpt)                          # token slots per block
+    kt = max(lpt // G, min(32 // G, 8))
+    if L <= 8192:
+        kt = max(lpt // G, min(kt, 4))
+    steps = -(-L // (tpb * kt * 64))
+    return steps * kt, steps * tpb * kt
+
+
 def bound(q, k, v, ref, scale, L, G, D):
     """Per-element error bound of the kernel's fp32 arithmetic (see above)."""
     kf = (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     vf = (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    tpb = 4 * (64 // (D // 8))                     # token slots per block
-    chunk = -(-(-(-L // 64)) // tpb) * tpb
-    dN = -(-chunk // tpb) + 8
+    kt, chunk = chunk_shape(G, D, L)
+    dN = kt + 8        # a slot's tokens, 3 shuffle levels, 4 waves
     dD = -(-chunk // 256) + 11
     H = q.shape[0]
     out = np.empty_like(ref)
@@ -70,14 +87,14 @@ def bound(q, k, v, ref, scale, L, G, D):
     return out
 
 
-def check(env, L, H=20, Hkv=5, D=128, seed=0, kscale=1.0, data=None):
+def check(env, L, H=20, Hkv=5, D=128, seed=0, kscale=1.0, data=None, ws=None):
     torch, tq, oracle = env
     print(f"attn L={L} H={H} Hkv={Hkv} D={D}", flush=True)
     q, k, v = make(L, H, Hkv, D, seed, kscale) if data is None else data
     qt = torch.from_numpy(q).cuda()
     kt = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda()
     vt = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
-    out = tq.tq_attn_decode(qt, kt, vt)
+    out = tq.tq_attn_decode(qt, kt, vt, workspace=ws)
     torch.cuda.synchronize()
     scale = np.float32(1.0 / np.sqrt(D))
     ref = oracle.attn_decode(q, k, v, scale)
@@ -88,14 +105,28 @@ def check(env, L, H=20, Hkv=5, D=128, seed=0, kscale=1.0, data=None):
     return qt, kt, vt, out
 
 
-@pytest.mark.parametrize("L", [1, 7, 16, 100, 2048, 2049, 8192, 32768])
+# here 64-token steps up to L = 8192 (one chunk up to 64 tokens, 64 chunks of
+# 2 steps at 8192), 128-token steps beyond (131072: 64 chunks of 16 steps)
+@pytest.mark.parametrize("L", [1, 7, 16, 64, 65, 100, 2048, 2049, 8192, 8193,
+                               32768, 131072])
 def test_attn_2b4t_heads(env, L):
     check(env, L, seed=L)
 
 
-@pytest.mark.parametrize("H,Hkv,D", [(8, 8, 128), (16, 8, 64), (32, 4, 128), (4, 1, 64)])
-def test_attn_group_sizes(env, H, Hkv, D):
-    check(env, 777, H, Hkv, D, seed=H + D)
+@pytest.mark.parametrize("L", [777, 5000])
+@pytest.mark.parametrize("H,Hkv,D", [(8, 8, 128), (16, 8, 64), (32, 4, 128), (4, 1, 64),
+                                     (64, 8, 128), (16, 2, 64)])
+def test_attn_group_sizes(env, H, Hkv, D, L):
+    check(env, L, H, Hkv, D, seed=H + D + L)
+
+
+def test_attn_workspace_reuse(env):
+    # one workspace across lengths with different chunk sizes and counts
+    torch, tq, _ = env
+    ws = tq.attn_workspace(20, 128, 40000, "cuda")
+    for i, L in enumerate([5000, 100, 40000, 1, 8193, 300]):
+        ws.fill_(0xFF)
+        check(env, L, seed=900 + i, ws=ws)
 
 
 def test_attn_peaked_scores(env):

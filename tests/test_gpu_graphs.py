@@ -1,6 +1,6 @@
 """Graph capture of the library calls that use scratch or several launches:
 tq_ternarize (a fill kernel clears its workspace, no memset node),
-tq_attn_decode (split + combine through a workspace) and the grouped
+tq_attn_decode (chunk pass + combine through a workspace) and the grouped
 quantize+GEMV.  Each graph is replayed several times with other eager work
 and synchronizations in between, and every replay must equal the eager
 result bit for bit.
@@ -68,11 +68,11 @@ def test_attn_graph(env):
     torch.cuda.synchronize()
     ref = ref.clone()
     out = torch.empty_like(ref)
-    ws = torch.empty(tq.attn_workspace_bytes(20, 128), dtype=torch.uint8, device="cuda")
+    ws = tq.attn_workspace(20, 128, 3000, "cuda")
     g = capture(torch, lambda: tq.tq_attn_decode(q, k, v, out=out, workspace=ws))
     for rep in range(4):
         out.fill_(7.0)
-        ws.fill_(0xFF)
+        ws.fill_(0xFF)  # any contents
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
