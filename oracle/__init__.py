@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "tqo_unpack": [p, i64, i64, p],
             "tqo_act_quant_f32": [p, i64, i64, p, p],
             "tqo_act_quant_bf16": [p, i64, i64, p, p],
+            "tqo_rmsnorm_act_quant_f32": [p, p, ctypes.c_float, i64, i64, p, p],
+            "tqo_rmsnorm_act_quant_bf16": [p, p, ctypes.c_float, i64, i64, p, p],
             "tqo_ternary_matmul": [p, p, i64, i64, i64, p],
             "tqo_ternary_matmul_rows": [p, p, i64, i64, i64, p, i64, p],
             "tqo_rescale_f32": [p, ctypes.c_float, p, i64, i64, p],
@@ -145,6 +147,30 @@ def act_quant(x, dtype: str = "bf16"):
     q = np.zeros((M, K), np.int8)
     s = np.zeros((M,), np.float32)
     _check(fn(_ptr(x), M, K, _ptr(q), _ptr(s) if M else None), "act_quant")
+    return q, s
+
+
+def rmsnorm_act_quant(x, gamma, eps: float, dtype: str = "bf16"):
+    """Sub-layer RMSNorm folded into per-row absmax quantization ([ISSUE]
+    "Architecture": norms before o_proj and down_proj).  ``x`` [M, K] and
+    ``gamma`` [K] are uint16 bf16 bit patterns (dtype 'bf16') or fp32.
+    Returns (q int8 [M, K], s_x fp32 [M]): q are the codes of x*gamma and
+    s_x = (a'/127) / sqrt(mean(x^2) + eps), so q * s_x approximates
+    RMSNorm(x) * gamma."""
+    dt = {"bf16": np.uint16, "f32": np.float32}[dtype]
+    x = _c(x, dt)
+    gamma = _c(gamma, dt).reshape(-1)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    M, K = x.shape
+    if gamma.size != K:
+        raise ValueError("gamma must have K entries")
+    q = np.zeros((M, K), np.int8)
+    s = np.zeros((M,), np.float32)
+    fn = (lib().tqo_rmsnorm_act_quant_bf16 if dtype == "bf16"
+          else lib().tqo_rmsnorm_act_quant_f32)
+    _check(fn(_ptr(x), _ptr(gamma), float(np.float32(eps)), M, K, _ptr(q),
+              _ptr(s) if M else None), "rmsnorm_act_quant")
     return q, s
 
 

@@ -123,6 +123,61 @@ int tqo_act_quant_bf16(const uint16_t *x, int64_t M, int64_t K,
 }
 
 /*
+ * Sub-layer RMSNorm folded into the quantization of one row ([ISSUE]
+ * "Architecture": sub-layer norms before o_proj and down_proj; "Diagnose"
+ * lists RMSNorm).  RMSNorm(x)_k = r * x_k * gamma_k with
+ * r = 1/sqrt(mean_k(x_k^2) + eps).  Absmax quantization gives the same codes
+ * for a row and for any positive multiple of it, so the codes are those of
+ * u = x*gamma (fp32 products) and r goes into the scale:
+ * s_x = (a'/127) * r, with a' the floored absmax of u.  mean(x^2) and r are
+ * formed in fp64 (each x^2 is exact there) and r is rounded once to fp32.
+ */
+static void rms_quant_row(const float *x, const float *gamma, int64_t K,
+                          float eps, int8_t *q, float *s_x, float *u)
+{
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; k++) {
+        u[k] = x[k] * gamma[k];             /* one fp32 rounding */
+        ss += (double)x[k] * (double)x[k];
+    }
+    float s_q;
+    quant_row(u, K, q, &s_q);
+    double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+    *s_x = s_q * (float)r;
+}
+
+int tqo_rmsnorm_act_quant_f32(const float *x, const float *gamma, float eps,
+                              int64_t M, int64_t K, int8_t *q, float *s_x)
+{
+    if (M < 0 || K <= 0 || !(eps > 0.0f)) return TQO_EARG;
+    if (M > 0 && (!x || !gamma || !q || !s_x)) return TQO_EARG;
+    float *u = (float *)malloc((size_t)K * sizeof(float));
+    if (!u) return TQO_EARG;
+    for (int64_t m = 0; m < M; m++)
+        rms_quant_row(x + m * K, gamma, K, eps, q + m * K, s_x + m, u);
+    free(u);
+    return TQO_OK;
+}
+
+int tqo_rmsnorm_act_quant_bf16(const uint16_t *x, const uint16_t *gamma,
+                               float eps, int64_t M, int64_t K, int8_t *q,
+                               float *s_x)
+{
+    if (M < 0 || K <= 0 || !(eps > 0.0f)) return TQO_EARG;
+    if (M > 0 && (!x || !gamma || !q || !s_x)) return TQO_EARG;
+    float *buf = (float *)malloc((size_t)K * 3 * sizeof(float));
+    if (!buf) return TQO_EARG;
+    float *row = buf, *g = buf + K, *u = buf + 2 * K;
+    for (int64_t k = 0; k < K; k++) g[k] = tqo_bf16_to_f32(gamma[k]);
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t k = 0; k < K; k++) row[k] = tqo_bf16_to_f32(x[m * K + k]);
+        rms_quant_row(row, g, K, eps, q + m * K, s_x + m, u);
+    }
+    free(buf);
+    return TQO_OK;
+}
+
+/*
  * The ternary product as its definition: every weight is decoded to
  * {-1,0,+1} and multiplied into an exact int64 sum.  [DIGEST] first item:
  * with weights in {-1,0,1} each product is an add, a subtract or nothing.

@@ -22,6 +22,8 @@
  *   - activations: per row, a = max|x|, a' = max(a, 1e-5f),
  *     inv = 127/a' (fp32), q = clamp(round-half-even(x*inv), -127, 127),
  *     s_x = a'/127 (fp32);
+ *   - sub-layer RMSNorm before quantizing: codes of u = x*gamma, and
+ *     s_x = (a'/127) * r, r = 1/sqrt(mean(x^2) + eps) in fp64 rounded once;
  *   - rescale: y = (float)acc * (s_w * s_x), each product rounded to fp32;
  *   - relu^2 gate: r = g > 0 ? g : 0,  h = (r*r)*u, in fp32.
  * The fp64 variants give the exact value of the same definition.
@@ -60,6 +62,16 @@ int tqo_act_quant_f32(const float *x, int64_t M, int64_t K,
                       int8_t *q, float *s_x);
 int tqo_act_quant_bf16(const uint16_t *x, int64_t M, int64_t K,
                        int8_t *q, float *s_x);
+
+/* RMSNorm(x) * gamma folded into the quantization of each row of x[M,K]:
+ * q = codes of u = x*gamma (fp32), s_x = (a'/127) * r with
+ * r = 1/sqrt(mean(x^2) + eps) (fp64, rounded once).  K > 0, eps > 0;
+ * gamma[K] has the dtype of x. */
+int tqo_rmsnorm_act_quant_f32(const float *x, const float *gamma, float eps,
+                              int64_t M, int64_t K, int8_t *q, float *s_x);
+int tqo_rmsnorm_act_quant_bf16(const uint16_t *x, const uint16_t *gamma,
+                               float eps, int64_t M, int64_t K, int8_t *q,
+                               float *s_x);
 
 /* acc[m,n] = sum_k W[n,k] * q[m,k], W decoded from packed[N/4,K]. */
 int tqo_ternary_matmul(const uint8_t *packed, const int8_t *q,
