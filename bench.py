@@ -336,12 +336,21 @@ def main():
     # ------------------------------------------------- per-kernel loops
     R = args.kernel_reps
 
-    def gemv_loop(name, start, fused):
+    # RMSNorm weights for the norm-fused variant (next-2: the sub-layer norm
+    # in the GEMV prologue), bf16 like the activations
+    gam = {name: (1.0 + 0.1 * torch.randn(K, device=dev)).to(torch.bfloat16)
+           for name, (N, K) in SHAPES.items()}
+
+    def gemv_loop(name, start, mode):
         P = pools[name]
         for r in range(R):
-            if fused:
+            if mode == "quant_gemv":
                 tq.tq_quant_gemv(x[name], P[(start + r) % len(P)], s_w, y[name],
                                  xq=xq[name], x_scale=xs[name])
+            elif mode == "rmsnorm_quant_gemv":
+                tq.tq_rmsnorm_quant_gemv(x[name], gam[name], P[(start + r) % len(P)],
+                                         s_w, eps=1e-5, y=y[name], xq=xq[name],
+                                         x_scale=xs[name])
             else:
                 tq.tq_gemv(P[(start + r) % len(P)], s_w, xq[name], xs[name], y[name])
 
@@ -350,12 +359,15 @@ def main():
         tq.tq_act_quant(x[name], xq[name], xs[name])
         nP = len(pools[name])
         row = {"N": N, "K": K}
-        for fused in (True, False):
-            gs = [timer.graph(lambda name=name, s=s, f=fused: gemv_loop(name, s, f))
+        for mode in ("quant_gemv", "gemv", "rmsnorm_quant_gemv"):
+            fused = mode != "gemv"
+            gs = [timer.graph(lambda name=name, s=s, m=mode: gemv_loop(name, s, m))
                   for s in range(0, nP, max(1, nP // 4))][:4]
             us = timer.time_graphs(gs, 8) * 1e3 / R
-            ab = algo_bytes_fused(N, K) if fused else algo_bytes(N, K)
-            row["quant_gemv" if fused else "gemv"] = {
+            # the norm-fused form also reads K gamma values (bf16)
+            ab = (algo_bytes_fused(N, K) + (2 * K if mode == "rmsnorm_quant_gemv" else 0)
+                  if fused else algo_bytes(N, K))
+            row[mode] = {
                 "us_per_launch": round(us, 3),
                 "weight_GBs": round(weight_bytes(N, K) / us / 1e3, 1),
                 "pct_hbm_peak": round(100 * weight_bytes(N, K) / us / 1e3 / HBM_PEAK_GBS, 1),

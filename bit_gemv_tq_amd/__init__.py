@@ -30,7 +30,7 @@ STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN",
 EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
            "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
            "tq_quant_gemv_group", "tq_ternarize", "tq_attn_decode",
-           "tq_status_string")
+           "tq_rmsnorm_act_quant", "tq_rmsnorm_quant_gemv", "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "tq_quant_gemv_group": [p, i32, i32, p, p, p, i64, p, p, p, p, p, p],
         "tq_ternarize": [p, i64, i64, p, p, p, p],
         "tq_attn_decode": [p, p, p, i64, i64, i64, i64, f32, p, p, ctypes.c_size_t, p],
+        "tq_rmsnorm_act_quant": [p, i32, p, f32, i64, i64, p, p, p],
+        "tq_rmsnorm_quant_gemv": [p, i32, p, f32, p, f32, i64, i64, p, p, p, p, p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -258,6 +260,56 @@ def tq_quant_gemv(x, packed, w_scale, y=None, acc=None, xq=None, x_scale=None,
     _check("tq_quant_gemv", lib.tq_quant_gemv(
         _ptr(x), xt, _ptr(packed), float(w_scale), N, K, _ptr(y), _ptr(acc),
         _ptr(xq), _ptr(x_scale), _ptr(y_scale), _stream(stream)))
+    return y
+
+
+def _gamma(gamma, x):
+    if gamma.dtype != x.dtype:
+        raise TypeError(f"gamma must have the dtype of x ({x.dtype}), got {gamma.dtype}")
+    _need(gamma, "gamma", x.dtype, x.device)
+    return gamma
+
+
+def tq_rmsnorm_act_quant(x, gamma, eps=1e-5, xq=None, x_scale=None, stream=None):
+    """Sub-layer RMSNorm folded into per-row absmax quantization: x bf16 or
+    fp32 [M, K] (or [K]), gamma [K] of the same dtype.  Returns (xq int8
+    [M, K], x_scale fp32 [M]) with xq * x_scale ~ RMSNorm(x) * gamma."""
+    torch = _torch()
+    xt = _raw_row(x)
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    M, K = x2.shape
+    _gamma(gamma, x)
+    if gamma.numel() != K:
+        raise ValueError(f"gamma has {gamma.numel()} elements, need K={K}")
+    xq = _out(xq, "xq", (M, K), torch.int8, x.device)
+    x_scale = _out(x_scale, "x_scale", (M,), torch.float32, x.device)
+    _check("tq_rmsnorm_act_quant", lib.tq_rmsnorm_act_quant(
+        _ptr(x2), xt, _ptr(gamma), float(eps), M, K, _ptr(xq), _ptr(x_scale),
+        _stream(stream)))
+    return xq, x_scale
+
+
+def tq_rmsnorm_quant_gemv(x, gamma, packed, w_scale, eps=1e-5, y=None, acc=None,
+                          xq=None, x_scale=None, stream=None):
+    """RMSNorm + act_quant + gemv at M = 1 in one launch.  x: bf16/fp32 [K],
+    gamma [K] of the same dtype.  Returns y; the quantized row and its scale
+    land in xq / x_scale (allocated when not given)."""
+    torch = _torch()
+    xt = _raw_row(x)
+    _gamma(gamma, x)
+    _need(packed, "packed", torch.uint8, x.device)
+    dev = packed.device
+    N, K = packed.shape[0] * 4, packed.shape[1]
+    if x.numel() != K or gamma.numel() != K:
+        raise ValueError(f"x and gamma need K={K} elements")
+    y = _out(y, "y", (N,), torch.float32, dev)
+    if acc is not None:
+        acc = _out(acc, "acc", (N,), torch.int32, dev)
+    xq = _out(xq, "xq", (K,), torch.int8, dev)
+    x_scale = _out(x_scale, "x_scale", (1,), torch.float32, dev)
+    _check("tq_rmsnorm_quant_gemv", lib.tq_rmsnorm_quant_gemv(
+        _ptr(x), xt, _ptr(gamma), float(eps), _ptr(packed), float(w_scale), N, K,
+        _ptr(y), _ptr(acc), _ptr(xq), _ptr(x_scale), _stream(stream)))
     return y
 
 

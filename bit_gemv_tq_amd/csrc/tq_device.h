@@ -209,6 +209,50 @@ __device__ __forceinline__ u32x4 quant_piece(const RawPiece<kBf16> &r,
   return q;
 }
 
+// ---------------------------------------------------------------- RMSNorm
+// Sub-layer RMSNorm folded into the quantization: the codes are those of
+// u = x * gamma (one fp32 rounding per value), and 1/sqrt(mean(x^2) + eps)
+// goes into the scale.  Value k (0..15) of a raw piece:
+template <bool kBf16>
+__device__ __forceinline__ float piece_value(const RawPiece<kBf16> &r, int k) {
+  if constexpr (kBf16) {
+    const uint32_t w = r.w[k / 8][(k % 8) / 2];
+    return __uint_as_float(k % 2 ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return __uint_as_float(r.w[k / 4][k % 4]);
+  }
+}
+
+// u = x * gamma for one piece, as an fp32 piece; adds sum(x^2) to `ss` in
+// fp64 (each square is exact there; fma and mul + add agree).
+template <bool kBf16>
+__device__ __forceinline__ RawPiece<false> scale_piece(const RawPiece<kBf16> &x,
+                                                       const RawPiece<kBf16> &g,
+                                                       double &ss) {
+#pragma clang fp contract(off)
+  RawPiece<false> u;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float xv = piece_value<kBf16>(x, k);
+    u.w[k / 4][k % 4] = __float_as_uint(xv * piece_value<kBf16>(g, k));
+    ss = fma((double)xv, (double)xv, ss);
+  }
+  return u;
+}
+
+// fp64 sum over a wave (xor butterfly: every lane ends with the same value,
+// since each step adds the same two partial sums in either order).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// The RMS factor, rounded once to fp32: 1 / sqrt(ss / K + eps) in fp64.
+__device__ __forceinline__ float rms_factor(double ss, int64_t K, float eps) {
+  return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+}
+
 // ---------------------------------------------------------------- epilogue
 // y = (float)acc * (s_w * s_x): two fp32 roundings, in this order.
 __device__ __forceinline__ float rescale(int acc, float c) {

@@ -194,7 +194,8 @@ tq_status launch_gemv_lds(const GemvPlan &pl, const GemvArgs &a, size_t lds,
 // 3 per CU (2 for the two-stream gate kernel).  Grids that give every team
 // exactly the same number of rows measured slower (all waves reach their
 // reductions at once), so the grid is not trimmed to a balanced count.
-RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate) {
+RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate,
+                      bool rms = false) {
   RegPlan pl{};
   int lpr = 16;
   while ((kp + lpr - 1) / lpr > 8) lpr *= 2;
@@ -207,8 +208,9 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate) {
   const int64_t teams = bt / lpr;
   int64_t blocks = (n4 + teams - 1) / teams;
   // Resident blocks per CU (persistent grid): 8-12 waves per CU, measured
-  // best on MI355X; the two-plane gate kernel holds more registers.
-  const int per_cu = bt == 512 ? (gate ? 1 : 2) : (gate ? 2 : 3);
+  // best on MI355X; the two-plane gate kernel and the RMSNorm prologue hold
+  // more registers (one 512-thread block per CU is what fits).
+  const int per_cu = bt == 512 ? (gate || rms ? 1 : 2) : (gate ? 2 : 3);
   const int64_t cap = (int64_t)num_cus * per_cu;
   if (blocks > cap) blocks = cap;
   pl.blocks = (int)(blocks < 1 ? 1 : blocks);
@@ -281,6 +283,28 @@ tq_status quant_gemv_m1(const void *x, tq_dtype xt, const uint8_t *p0,
   if (N == 0) return TQ_OK;
   return gemv_m1(p0, s0, p1, s1, xq, y_scale ? y_scale : x_scale, N, K, y,
                  acc0, acc1, stream);
+}
+
+// The same with the sub-layer RMSNorm folded into the quantization.
+tq_status rmsnorm_quant_gemv_m1(const void *x, tq_dtype xt, const void *gamma,
+                                float eps, const uint8_t *p0, float s0, int64_t N,
+                                int64_t K, float *y, int32_t *acc0, int8_t *xq,
+                                float *x_scale, hipStream_t stream) {
+  DeviceInfo dev;
+  if (tq_status s = current_device(&dev)) return s;
+  const int64_t n4 = N / 4, kp = K / 16;
+  if (N > 0 && kp <= kRegMaxPieces) {  // kp >= 1: K > 0 is required
+    RegArgs a{p0, nullptr, s0,   0.0f, nullptr, nullptr, (int)n4, (int)kp,
+              y,  acc0,    nullptr, x, xq,      x_scale, nullptr};
+    a.gamma = gamma;
+    a.eps = eps;
+    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, false, true), false,
+                           xt == TQ_BF16 ? kXBf16Rms : kXF32Rms, a, stream);
+  }
+  if (tq_status s = rmsnorm_act_quant(x, xt, gamma, eps, 1, K, xq, x_scale, stream))
+    return s;
+  if (N == 0) return TQ_OK;
+  return gemv_m1(p0, s0, nullptr, 0.0f, xq, x_scale, N, K, y, acc0, nullptr, stream);
 }
 
 tq_status check_quant_args(const void *x, tq_dtype xt, const uint8_t *p,
@@ -384,6 +408,21 @@ extern "C" tq_status tq_quant_gemv(const void *x, tq_dtype xt,
     return s;
   return quant_gemv_m1(x, xt, packed, w_scale, nullptr, 0.0f, N, K, y, acc,
                        nullptr, xq, x_scale, y_scale, stream);
+}
+
+extern "C" tq_status tq_rmsnorm_quant_gemv(const void *x, tq_dtype xt,
+                                           const void *gamma, float eps,
+                                           const uint8_t *packed, float w_scale,
+                                           int64_t N, int64_t K, float *y,
+                                           int32_t *acc, int8_t *xq,
+                                           float *x_scale, hipStream_t stream) {
+  using namespace tq;
+  if (tq_status s = check_quant_args(x, xt, packed, N, K, y, acc, nullptr, xq,
+                                     x_scale, nullptr))
+    return s;
+  if (tq_status s = check_rms(gamma, eps, K)) return s;
+  return rmsnorm_quant_gemv_m1(x, xt, gamma, eps, packed, w_scale, N, K, y, acc,
+                               xq, x_scale, stream);
 }
 
 extern "C" tq_status tq_quant_gate_up_relu2(

@@ -37,8 +37,12 @@ constexpr int reg_block_threads(int lpr) { return lpr >= 256 ? 512 : kRegThreads
 constexpr int kRegMaxPieces = 2048;  // K <= 32768 bytes
 
 // Activation forms: kXInt8 = int8 row + scale given (tq_gemv); kXBf16 /
-// kXF32 = raw row, quantized in the prologue (tq_quant_gemv).
-constexpr int kXInt8 = 0, kXBf16 = 1, kXF32 = 2;
+// kXF32 = raw row, quantized in the prologue (tq_quant_gemv); kXBf16Rms /
+// kXF32Rms = raw row with the sub-layer RMSNorm folded into that
+// quantization (tq_rmsnorm_quant_gemv).
+constexpr int kXInt8 = 0, kXBf16 = 1, kXF32 = 2, kXBf16Rms = 3, kXF32Rms = 4;
+constexpr bool xt_rms(int xt) { return xt == kXBf16Rms || xt == kXF32Rms; }
+constexpr bool xt_bf16(int xt) { return xt == kXBf16 || xt == kXBf16Rms; }
 
 // Grouped form: several weight matrices with the same K that read one
 // activation row (e.g. the q, k and v projections), run as one packed-row
@@ -70,6 +74,8 @@ struct RegArgs {
   const float *y_scale;  // optional [1]: activation scale used in the
                          // rescale instead of s_x (raw forms)
   RegSegs seg;           // grouped form (not with kGate); n4 = total rows
+  const void *gamma;     // [K] RMSNorm weights, dtype of x (kX*Rms)
+  float eps;             // RMSNorm epsilon (kX*Rms)
 };
 
 // Segment of global packed row i (grouped form): its first row and index.
@@ -102,10 +108,13 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   constexpr int SPAN = NP * LPR;                      // pieces a team covers
   constexpr int SP = (SPAN + BT - 1) / BT;  // staging loads
   static_assert(NP >= 1 && SPAN <= kRegMaxPieces, "pieces per lane");
-  constexpr int VPP = XT == kXInt8 ? 1 : (XT == kXBf16 ? 2 : 4);  // words/piece
+  constexpr int VPP = XT == kXInt8 ? 1 : (xt_bf16(XT) ? 2 : 4);  // words/piece
+  constexpr bool kRms = xt_rms(XT);
+  constexpr int GPP = kRms ? VPP : 1;  // gamma words per piece (unused: 1)
   __shared__ u32x4 x_lds[SP * BT];  // padded: stores unconditional
   __shared__ int red[2][BT / kWave][NM][4];
   __shared__ float amax_lds[BT / kWave];
+  __shared__ double ss_lds[kRms ? BT / kWave : 1];
 
   const int kp = g.kp, n4 = g.n4;
   const int lane = threadIdx.x % LPR;
@@ -131,12 +140,18 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   const u32x4 *xg = reinterpret_cast<const u32x4 *>(
       XT == kXInt8 ? static_cast<const void *>(g.xq) : g.x);
   u32x4 xs[SP][VPP];
+  u32x4 gs[SP][GPP];  // RMSNorm weights of the same pieces (kRms)
 #pragma unroll
   for (int s = 0; s < SP; ++s) {
     const int p = (int)threadIdx.x + s * BT;
     const int pc = EXACT ? min(p, SPAN - 1) : min(p, kp - 1);
 #pragma unroll
     for (int v = 0; v < VPP; ++v) xs[s][v] = xg[pc * VPP + v];
+    if constexpr (kRms) {
+#pragma unroll
+      for (int v = 0; v < VPP; ++v)
+        gs[s][v] = reinterpret_cast<const u32x4 *>(g.gamma)[pc * VPP + v];
+    }
   }
   // Keep the scheduler from sinking these loads below the weight loads.
   __builtin_amdgcn_sched_barrier(0);
@@ -170,33 +185,65 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
     sx = g.x_scale[0];
   } else {
     // Per-token absmax over the whole row (every block, redundantly), then
-    // q = rne(x * (127/a')) exactly as tq_act_quant.
-    constexpr bool kBf16 = XT == kXBf16;
+    // q = rne(x * (127/a')) exactly as tq_act_quant.  With the RMSNorm
+    // folded in, the same on u = x * gamma, and s_x = (a'/127) * r with
+    // r = 1/sqrt(mean(x^2) + eps): every block sums the squares in the same
+    // order, so all get the same r.
+    constexpr bool kBf16 = xt_bf16(XT);
     auto raw = [&](int s) {
       RawPiece<kBf16> r;
 #pragma unroll
       for (int v = 0; v < VPP; ++v) r.w[v] = xs[s][v];
       return r;
     };
+    // Values that are quantized: the raw row, or u = x * gamma (fp32).
+    using QPiece = RawPiece<kRms ? false : kBf16>;
+    QPiece qv[SP];
+    double ss = 0.0;
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      if constexpr (kRms) {
+        RawPiece<kBf16> gr;
+#pragma unroll
+        for (int v = 0; v < VPP; ++v) gr.w[v] = gs[s][v];
+        double sq = 0.0;
+        qv[s] = scale_piece<kBf16>(raw(s), gr, sq);
+        // slots past the row end re-read an in-row piece: not summed again
+        if ((int)threadIdx.x + s * BT < kp) ss += sq;
+      } else {
+        qv[s] = raw(s);
+      }
+    }
+    constexpr bool kQBf16 = kRms ? false : kBf16;
     // Slots past the row end hold a re-read of an in-row piece (clamped
     // index), so they cannot change the maximum.
     uint32_t mb = 0;
 #pragma unroll
-    for (int s = 0; s < SP; ++s) mb = absmax_bits<kBf16>(raw(s), mb);
-    float a = wave_max(absmax_value<kBf16>(mb));
+    for (int s = 0; s < SP; ++s) mb = absmax_bits<kQBf16>(qv[s], mb);
+    float a = wave_max(absmax_value<kQBf16>(mb));
     if ((threadIdx.x & (kWave - 1)) == 0) amax_lds[wave] = a;
+    if constexpr (kRms) {
+      ss = wave_sum_f64(ss);
+      if ((threadIdx.x & (kWave - 1)) == 0) ss_lds[wave] = ss;
+    }
     __syncthreads();
     a = amax_lds[0];
 #pragma unroll
     for (int w = 1; w < BT / kWave; ++w) a = fmaxf(a, amax_lds[w]);
     const float ap = a > 1e-5f ? a : 1e-5f;
     const float inv = 127.0f / ap;  // correctly rounded fp32 division
-    const float s_x = ap / 127.0f;
+    float s_x = ap / 127.0f;
+    if constexpr (kRms) {
+      double t = ss_lds[0];
+#pragma unroll
+      for (int w = 1; w < BT / kWave; ++w) t += ss_lds[w];
+      s_x = s_x * rms_factor(t, (int64_t)kp * 16, g.eps);
+    }
     const bool writer = blockIdx.x == 0;
 #pragma unroll
     for (int s = 0; s < SP; ++s) {
       const int p = (int)threadIdx.x + s * BT;
-      const u32x4 q = quant_piece<kBf16>(raw(s), inv);
+      const u32x4 q = quant_piece<kQBf16>(qv[s], inv);
       x_lds[threadIdx.x + s * BT] = q;
       if (writer && p < kp)
         reinterpret_cast<u32x4 *>(g.xq_out)[p] = q;
@@ -334,12 +381,31 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
   }                                                                            \
   return TQ_ERR_DTYPE;
 
+// The RMSNorm forms exist for the plain GEMV only.
+#define TQ_REG_XT_CASES_RMS(LPR)                                               \
+  switch (xt) {                                                                \
+    case kXInt8: { TQ_REG_NP_CASES(LPR, false, kXInt8) }                       \
+    case kXBf16: { TQ_REG_NP_CASES(LPR, false, kXBf16) }                       \
+    case kXF32: { TQ_REG_NP_CASES(LPR, false, kXF32) }                         \
+    case kXBf16Rms: { TQ_REG_NP_CASES(LPR, false, kXBf16Rms) }                 \
+    case kXF32Rms: { TQ_REG_NP_CASES(LPR, false, kXF32Rms) }                   \
+  }                                                                            \
+  return TQ_ERR_DTYPE;
+
 #define TQ_DEFINE_LAUNCH_REG(LPR, GATE)                                        \
   template <>                                                                  \
   tq_status launch_reg_part<LPR, GATE>(const RegPlan &pl, int xt,              \
                                        const RegArgs &a, hipStream_t s) {      \
     const dim3 grid(pl.blocks), block(reg_block_threads(LPR));                 \
     TQ_REG_XT_CASES(LPR, GATE)                                                 \
+  }
+
+#define TQ_DEFINE_LAUNCH_REG_GEMV(LPR)                                         \
+  template <>                                                                  \
+  tq_status launch_reg_part<LPR, false>(const RegPlan &pl, int xt,             \
+                                        const RegArgs &a, hipStream_t s) {     \
+    const dim3 grid(pl.blocks), block(reg_block_threads(LPR));                 \
+    TQ_REG_XT_CASES_RMS(LPR)                                                   \
   }
 
 template <int LPR, bool GATE>

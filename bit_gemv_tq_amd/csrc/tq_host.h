@@ -52,6 +52,13 @@ tq_status launch(void (*kernel)(Params...), dim3 grid, dim3 block,
   return call(static_cast<Params>(args)...);
 }
 
+// RMSNorm-folded quantization of M rows (tq_act_quant.hip), used by the
+// fused GEMV's fallback; check_rms validates gamma, eps and K for both.
+tq_status rmsnorm_act_quant(const void *x, tq_dtype xt, const void *gamma, float eps,
+                            int64_t M, int64_t K, int8_t *xq, float *x_scale,
+                            hipStream_t stream);
+tq_status check_rms(const void *gamma, float eps, int64_t K);
+
 // Allow dynamic LDS above the default limit for `kernel` (once per process
 // and kernel; harmless when the request is below the default).
 tq_status allow_dynamic_lds(const void *kernel, int bytes);

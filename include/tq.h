@@ -175,6 +175,43 @@ TQ_API tq_status tq_quant_gemv(const void *x, tq_dtype xt,
                                hipStream_t stream);
 
 /*
+ * tq_rmsnorm_act_quant -- the sub-layer RMSNorm folded into the per-token
+ * quantization ([ISSUE] "Architecture": norms before o_proj and down_proj;
+ * RMSNorm(x)_k = x_k * gamma_k / sqrt(mean(x^2) + eps)).  Absmax
+ * quantization gives the same codes for any positive multiple of a row, so
+ * the codes are those of u = x * gamma (fp32 products) and the RMS factor
+ * goes into the scale:
+ *   xq[m,:]    = the tq_act_quant codes of u[m,:]
+ *   x_scale[m] = (a'/127) * r,  r = 1/sqrt(mean_k x[m,k]^2 + eps), the mean
+ *                and r formed in fp64 and r rounded once to fp32.
+ * xq * x_scale approximates RMSNorm(x) * gamma.  The codes are exact
+ * decisions; x_scale depends on the order in which the squares are summed
+ * only in its last bit, rarely.
+ *   x, xq, x_scale, M  as tq_act_quant.
+ *   gamma    [K], the dtype of x, 16-B aligned (device).
+ *   eps      > 0 and finite.
+ *   K        > 0 (an empty row has no mean).
+ */
+TQ_API tq_status tq_rmsnorm_act_quant(const void *x, tq_dtype xt, const void *gamma,
+                                      float eps, int64_t M, int64_t K, int8_t *xq,
+                                      float *x_scale, hipStream_t stream);
+
+/*
+ * tq_rmsnorm_quant_gemv -- tq_rmsnorm_act_quant followed by tq_gemv at
+ * M = 1 in one launch: the RMSNorm and the quantization run in the GEMV
+ * prologue (every block recomputes the row's absmax and sum of squares in
+ * the same order).  Arguments as tq_quant_gemv (no y_scale: y uses the
+ * row's own x_scale) plus gamma and eps as tq_rmsnorm_act_quant.  Codes and
+ * acc equal those of the two calls exactly; x_scale and y may differ from
+ * theirs in the last bit, rarely (the squares are summed in another order).
+ * K > 32768 takes two launches internally.
+ */
+TQ_API tq_status tq_rmsnorm_quant_gemv(const void *x, tq_dtype xt, const void *gamma,
+                                       float eps, const uint8_t *packed, float w_scale,
+                                       int64_t N, int64_t K, float *y, int32_t *acc,
+                                       int8_t *xq, float *x_scale, hipStream_t stream);
+
+/*
  * tq_quant_gate_up_relu2 -- tq_act_quant followed by tq_gate_up_relu2 at
  * M = 1 in one launch; arguments as tq_quant_gemv and tq_gate_up_relu2.
  */

@@ -33,7 +33,8 @@ def test_header_declares_the_calls():
     assert set(names) == {"tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
                           "tq_gate_up_relu2", "tq_quant_gemv",
                           "tq_quant_gate_up_relu2", "tq_quant_gemv_group",
-                          "tq_ternarize", "tq_attn_decode", "tq_status_string"}
+                          "tq_ternarize", "tq_attn_decode", "tq_rmsnorm_act_quant",
+                          "tq_rmsnorm_quant_gemv", "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -92,6 +93,31 @@ def test_act_quant_validation(tq):
     assert f(MIS, 0, 1, 64, A, A, None) == ALIGN
     assert f(A, 0, 1, 64, MIS, A, None) == ALIGN
     assert f(A, 0, 0, 64, A, A, None) == OK
+
+
+def test_rmsnorm_validation(tq):
+    f = tq.lib.tq_rmsnorm_act_quant
+    #        x  xt gamma eps     M   K  xq  xs stream
+    assert f(A, 2, A, 1e-5, 1, 64, A, A, None) == DTYPE
+    assert f(A, 0, A, 0.0, 1, 64, A, A, None) == SHAPE          # eps > 0
+    assert f(A, 0, A, -1e-5, 1, 64, A, A, None) == SHAPE
+    assert f(A, 0, A, float("inf"), 1, 64, A, A, None) == SHAPE
+    assert f(A, 0, A, float("nan"), 1, 64, A, A, None) == SHAPE
+    assert f(A, 0, A, 1e-5, 1, 0, A, A, None) == SHAPE          # K > 0
+    assert f(A, 0, None, 1e-5, 1, 64, A, A, None) == NULL
+    assert f(A, 0, MIS, 1e-5, 1, 64, A, A, None) == ALIGN
+    assert f(A, 0, A, 1e-5, 65, 64, A, A, None) == SHAPE
+    g = tq.lib.tq_rmsnorm_quant_gemv
+    #        x  xt gamma eps  packed  ws   N   K   y  acc  xq  xs stream
+    assert g(A, 3, A, 1e-5, A, 0.02, 64, 64, A, None, A, A, None) == DTYPE
+    assert g(A, 0, A, 1e-5, A, 0.02, 62, 64, A, None, A, A, None) == SHAPE
+    assert g(A, 0, A, 1e-5, A, 0.02, 64, 0, A, None, A, A, None) == SHAPE
+    assert g(A, 0, A, 0.0, A, 0.02, 64, 64, A, None, A, A, None) == SHAPE
+    assert g(A, 0, None, 1e-5, A, 0.02, 64, 64, A, None, A, A, None) == NULL
+    assert g(A, 0, A, 1e-5, None, 0.02, 64, 64, A, None, A, A, None) == NULL
+    assert g(A, 0, A, 1e-5, A, 0.02, 64, 64, A, None, None, A, None) == NULL
+    assert g(A, 0, MIS, 1e-5, A, 0.02, 64, 64, A, None, A, A, None) == ALIGN
+    assert g(A, 0, A, 1e-5, A, 0.02, 64, 64, A, None, MIS, A, None) == ALIGN
 
 
 def test_gemm_small_and_gate_validation(tq):
@@ -225,6 +251,9 @@ def test_no_device_is_reported(tq):
     assert tq.lib.tq_act_quant(A, 0, 1, 64, A, A, None) == DEVICE
     assert tq.lib.tq_pack(A, 8, 16, A, None) == DEVICE
     assert tq.lib.tq_ternarize(A, 8, 16, A, A, A, None) == DEVICE
+    assert tq.lib.tq_rmsnorm_act_quant(A, 0, A, 1e-5, 1, 64, A, A, None) == DEVICE
+    assert tq.lib.tq_rmsnorm_quant_gemv(A, 0, A, 1e-5, A, 0.02, 64, 64, A, None, A, A,
+                                        None) == DEVICE
     assert tq.lib.tq_attn_decode(A, A, A, 20, 5, 128, 16, 0.1, A, A,
                                  tq.attn_workspace_bytes(20, 128, 16), None) == DEVICE
     assert tq.lib.tq_gemm_small(A, 0.02, A, A, 4, 64, 64, A, None, None) == DEVICE
