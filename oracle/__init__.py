@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         sig = {
             "tqo_pack": [p, i64, i64, p],
             "tqo_unpack": [p, i64, i64, p],
+            "tqo_pack3": [p, i64, i64, p],
+            "tqo_unpack3": [p, i64, i64, p],
             "tqo_act_quant_f32": [p, i64, i64, p, p],
             "tqo_act_quant_bf16": [p, i64, i64, p, p],
             "tqo_rmsnorm_act_quant_f32": [p, p, ctypes.c_float, i64, i64, p, p],
@@ -126,6 +128,26 @@ def unpack(packed, N: int) -> np.ndarray:
     K = packed.shape[1]
     out = np.zeros((N, K), np.int8)
     _check(lib().tqo_unpack(_ptr(packed), N, K, _ptr(out)), "unpack")
+    return out
+
+
+def pack3(w) -> np.ndarray:
+    """int8 weights [N, K] in {-1,0,1} -> uint8 [ceil(N/5), K], five weights
+    per byte (base 3, stored as ceil(256 v / 243))."""
+    w = _c(w, np.int8)
+    N, K = w.shape
+    out = np.zeros(((N + 4) // 5, K), np.uint8)
+    _check(lib().tqo_pack3(_ptr(w), N, K, _ptr(out)), "pack3")
+    return out
+
+
+def unpack3(packed, N: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    K = packed.shape[1]
+    if packed.shape[0] != (N + 4) // 5:
+        raise ValueError(f"packed has {packed.shape[0]} rows, need ceil({N}/5)")
+    out = np.zeros((N, K), np.int8)
+    _check(lib().tqo_unpack3(_ptr(packed), N, K, _ptr(out)), "unpack3")
     return out
 
 

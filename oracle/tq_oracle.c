@@ -71,6 +71,67 @@ int tqo_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *w)
 }
 
 /*
+ * Denser packing: five ternary weights per byte, 1.6 bits per weight (the
+ * page "1bit.systems" README names the "TQ1_0" family only; no layout is
+ * given).  Reading used here: the packed array is [N5, K] with
+ * N5 = ceil(N/5); byte [i,k] holds rows j*N5 + i (j = 0..4) of column k as
+ * the base-3 number v = sum_j c_j 3^j of their codes c = w + 1 (rows past N
+ * are zero weights, c = 1), stored as the byte q = ceil(256 v / 243).  v is
+ * recovered as floor(243 q / 256); bytes that are not the image of some v
+ * (13 of the 256) are reserved.
+ */
+static int64_t n5_of(int64_t N) { return (N + 4) / 5; }
+
+int tqo_pack3(const int8_t *w, int64_t N, int64_t K, uint8_t *packed)
+{
+    if (N < 0 || K < 0) return TQO_EARG;
+    const int64_t n5 = n5_of(N);
+    if ((n5 > 0 && K > 0) && (!w || !packed)) return TQO_EARG;
+    for (int64_t i = 0; i < n5; i++) {
+        for (int64_t k = 0; k < K; k++) {
+            unsigned v = 0, p3 = 1;
+            for (int j = 0; j < 5; j++) {
+                int64_t n = j * n5 + i;
+                int c = 1;                      /* padding row: weight 0 */
+                if (n < N) {
+                    int wv = w[n * K + k];
+                    if (wv < -1 || wv > 1) return TQO_ECODE;
+                    c = wv + 1;
+                }
+                v += (unsigned)c * p3;
+                p3 *= 3;
+            }
+            packed[i * K + k] = (uint8_t)((v * 256 + 242) / 243);
+        }
+    }
+    return TQO_OK;
+}
+
+int tqo_unpack3(const uint8_t *packed, int64_t N, int64_t K, int8_t *w)
+{
+    if (N < 0 || K < 0) return TQO_EARG;
+    const int64_t n5 = n5_of(N);
+    if ((n5 > 0 && K > 0) && (!w || !packed)) return TQO_EARG;
+    for (int64_t i = 0; i < n5; i++) {
+        for (int64_t k = 0; k < K; k++) {
+            unsigned q = packed[i * K + k];
+            unsigned v = (q * 243) >> 8;
+            if ((v * 256 + 242) / 243 != q) return TQO_ECODE;   /* reserved */
+            for (int j = 0; j < 5; j++) {
+                int c = (int)(v % 3);
+                v /= 3;
+                int64_t n = j * n5 + i;
+                if (n < N)
+                    w[n * K + k] = (int8_t)(c - 1);
+                else if (c != 1)
+                    return TQO_ECODE;                        /* padding not zero */
+            }
+        }
+    }
+    return TQO_OK;
+}
+
+/*
  * Per-token absmax quantization to int8 of one row of K fp32 values.
  * Decision arithmetic is fp32, as in the kernel that takes the same decision.
  */

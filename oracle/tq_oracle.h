@@ -57,6 +57,12 @@ int tqo_pack(const int8_t *w, int64_t N, int64_t K, uint8_t *packed);
 /* Inverse of tqo_pack: packed[N/4,K] -> w[N,K]. */
 int tqo_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *w);
 
+/* Five weights per byte: w[N,K] -> packed[ceil(N/5),K]; byte [i,k] holds rows
+ * j*ceil(N/5)+i as q = ceil(256 v/243), v = sum_j (w+1) 3^j (rows past N are
+ * zero weights).  Unpack rejects reserved bytes and nonzero padding. */
+int tqo_pack3(const int8_t *w, int64_t N, int64_t K, uint8_t *packed);
+int tqo_unpack3(const uint8_t *packed, int64_t N, int64_t K, int8_t *w);
+
 /* Per-row absmax int8 quantization of x[M,K] (fp32 or bf16 bit patterns). */
 int tqo_act_quant_f32(const float *x, int64_t M, int64_t K,
                       int8_t *q, float *s_x);
