@@ -514,6 +514,39 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
     log(f"gemv q_proj: {rows['gemv_q_proj_2560x2560']}")
     del P
 
+    # next-3: the five-weights-per-byte layout (tq_gemv3) at the metric's
+    # shapes, beside the two-bit int8 GEMV timed above
+    g3 = {}
+    for name, (N, K) in SHAPES.items():
+        n5 = (N + 4) // 5
+        b3 = n5 * K
+        copies = max(4, -(-(640 << 20) // b3))
+        P3 = []
+        for c in range(copies):
+            w = workloads.ternary_codes_torch(N, K, seed=96000 + c, device=dev)
+            P3.append(tq.tq_pack3(w))
+            del w
+        xb = workloads.activations_bf16(1, K, seed=97)
+        xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, s = tq.tq_act_quant(xt)
+        y3 = torch.empty(N, dtype=torch.float32, device=dev)
+
+        def f3(st, P3=P3, q=q, s=s, y3=y3, N=N):
+            for r in range(R):
+                tq.tq_gemv3(P3[(st + r) % len(P3)], 0.02, q[0], s, N, y3)
+        us = loop_us(f3, len(P3))
+        two_bit = per_shape[name]["gemv"]["us_per_launch"]
+        g3[name] = {
+            "us_per_launch": round(us, 3),
+            "packed_bytes": b3,
+            "packed_GBs": round(b3 / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * (b3 + K + 4 + 4 * N) / us / 1e3 / HBM_PEAK_GBS, 1),
+            "tweights_per_s": round(N * K / us / 1e6, 2),
+            "speedup_vs_2bit_gemv": round(two_bit / us, 3)}
+        log(f"gemv3 {name}: {g3[name]}")
+        del P3
+    rows["gemv3_five_per_byte"] = g3
+
     # a4: fused gate/up + relu^2, M = 1 (2B-4T MLP)
     N, K = workloads.INTERMEDIATE, workloads.HIDDEN
     pg = pool_of(N, K, 320 << 20, 91000)

@@ -30,7 +30,8 @@ STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_ALIGN",
 EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
            "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
            "tq_quant_gemv_group", "tq_ternarize", "tq_attn_decode",
-           "tq_rmsnorm_act_quant", "tq_rmsnorm_quant_gemv", "tq_status_string")
+           "tq_rmsnorm_act_quant", "tq_rmsnorm_quant_gemv", "tq_pack3", "tq_gemv3",
+           "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -61,6 +62,8 @@ def _load() -> ctypes.CDLL:
         "tq_ternarize": [p, i64, i64, p, p, p, p],
         "tq_attn_decode": [p, p, p, i64, i64, i64, i64, f32, p, p, ctypes.c_size_t, p],
         "tq_rmsnorm_act_quant": [p, i32, p, f32, i64, i64, p, p, p],
+        "tq_pack3": [p, i64, i64, p, p],
+        "tq_gemv3": [p, f32, p, p, i64, i64, p, p, p],
         "tq_rmsnorm_quant_gemv": [p, i32, p, f32, p, f32, i64, i64, p, p, p, p, p],
     }
     for name, args in sigs.items():
@@ -135,6 +138,36 @@ def tq_pack(w, packed=None, stream=None):
     packed = _out(packed, "packed", (N // 4, K), torch.uint8, w.device)
     _check("tq_pack", lib.tq_pack(_ptr(w), N, K, _ptr(packed), _stream(stream)))
     return packed
+
+
+def tq_pack3(w, packed=None, stream=None):
+    """int8 ternary weights [N, K] -> uint8 [ceil(N/5), K], five weights per
+    byte (the denser layout of tq_gemv3)."""
+    torch = _torch()
+    _need(w, "w", torch.int8)
+    N, K = w.shape
+    packed = _out(packed, "packed", ((N + 4) // 5, K), torch.uint8, w.device)
+    _check("tq_pack3", lib.tq_pack3(_ptr(w), N, K, _ptr(packed), _stream(stream)))
+    return packed
+
+
+def tq_gemv3(packed, w_scale, xq, x_scale, N, y=None, acc=None, stream=None):
+    """tq_gemv on the five-per-byte layout (packed [ceil(N/5), K]); returns y."""
+    torch = _torch()
+    _need(packed, "packed", torch.uint8)
+    dev = packed.device
+    K = packed.shape[1]
+    if packed.shape[0] != (N + 4) // 5:
+        raise ValueError(f"packed has {packed.shape[0]} rows, need ceil({N}/5)")
+    _need(xq, "xq", torch.int8, dev)
+    _need(x_scale, "x_scale", torch.float32, dev)
+    y = _out(y, "y", (N,), torch.float32, dev)
+    if acc is not None:
+        acc = _out(acc, "acc", (N,), torch.int32, dev)
+    _check("tq_gemv3", lib.tq_gemv3(_ptr(packed), float(w_scale), _ptr(xq),
+                                    _ptr(x_scale), N, K, _ptr(y), _ptr(acc),
+                                    _stream(stream)))
+    return y
 
 
 def tq_act_quant(x, xq=None, x_scale=None, stream=None):

@@ -100,6 +100,33 @@ TQ_API tq_status tq_pack(const int8_t *w, int64_t N, int64_t K, uint8_t *packed,
                   hipStream_t stream);
 
 /*
+ * tq_pack3 -- the denser layout: five weights per byte, 1.6 bits per weight
+ * ([README] names the "TQ1_0" family of such formats only; the layout is
+ * this library's reading).  packed [N5, K], N5 = ceil(N/5); byte [i,k]
+ * holds rows j*N5 + i (j = 0..4) of column k as the base-3 number
+ * v = sum_j (w+1) 3^j (rows past N count as zero weights), stored as
+ * q = ceil(256 v / 243).  13 byte values encode no v and are reserved.
+ *   w       int8 [N,K], values in {-1,0,1}, 16-B aligned; any other value
+ *           makes its byte the reserved value 1 (outside the contract of
+ *           tq_gemv3).
+ *   packed  uint8 [ceil(N/5), K], output, 16-byte aligned.
+ * K % 16 == 0; any N >= 0.
+ */
+TQ_API tq_status tq_pack3(const int8_t *w, int64_t N, int64_t K, uint8_t *packed,
+                          hipStream_t stream);
+
+/*
+ * tq_gemv3 -- tq_gemv on the tq_pack3 layout: the same exact sums and the
+ * same fp32 outputs, bit for bit, reading 20% fewer weight bytes.
+ *   packed   uint8 [ceil(N/5), K] from tq_pack3 (16-B aligned), w_scale = s_w.
+ *   xq, x_scale, y, acc  as tq_gemv.
+ * 16 <= K <= 32768, K % 16 == 0; N >= 0 (N = 0: nothing is written).
+ */
+TQ_API tq_status tq_gemv3(const uint8_t *packed, float w_scale, const int8_t *xq,
+                          const float *x_scale, int64_t N, int64_t K, float *y,
+                          int32_t *acc, hipStream_t stream);
+
+/*
  * tq_act_quant -- per-token absmax int8 quantization of activations
  * (the conventions above).
  *   x        [M,K] bf16 (xt = TQ_BF16) or fp32 (xt = TQ_F32), 16-B aligned.

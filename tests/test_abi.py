@@ -34,7 +34,8 @@ def test_header_declares_the_calls():
                           "tq_gate_up_relu2", "tq_quant_gemv",
                           "tq_quant_gate_up_relu2", "tq_quant_gemv_group",
                           "tq_ternarize", "tq_attn_decode", "tq_rmsnorm_act_quant",
-                          "tq_rmsnorm_quant_gemv", "tq_status_string"}
+                          "tq_rmsnorm_quant_gemv", "tq_pack3", "tq_gemv3",
+                          "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -118,6 +119,26 @@ def test_rmsnorm_validation(tq):
     assert g(A, 0, A, 1e-5, A, 0.02, 64, 64, A, None, None, A, None) == NULL
     assert g(A, 0, MIS, 1e-5, A, 0.02, 64, 64, A, None, A, A, None) == ALIGN
     assert g(A, 0, A, 1e-5, A, 0.02, 64, 64, A, None, MIS, A, None) == ALIGN
+
+
+def test_pack3_gemv3_validation(tq):
+    f = tq.lib.tq_pack3
+    assert f(A, 7, 8, A, None) == SHAPE            # K % 16
+    assert f(A, -1, 16, A, None) == SHAPE
+    assert f(None, 7, 16, A, None) == NULL
+    assert f(A, 7, 16, MIS, None) == ALIGN
+    assert f(A, 0, 16, A, None) == OK
+    g = tq.lib.tq_gemv3
+    #        packed ws  xq xs  N   K   y  acc stream
+    assert g(A, 0.02, A, A, 7, 8, A, None, None) == SHAPE
+    assert g(A, 0.02, A, A, 7, 0, A, None, None) == SHAPE       # K >= 16
+    assert g(A, 0.02, A, A, 7, 32784, A, None, None) == SHAPE   # K <= 32768
+    assert g(A, 0.02, A, A, -5, 16, A, None, None) == SHAPE
+    assert g(None, 0.02, A, A, 7, 16, A, None, None) == NULL
+    assert g(A, 0.02, A, A, 7, 16, None, None, None) == NULL
+    assert g(A, 0.02, MIS, A, 7, 16, A, None, None) == ALIGN
+    assert g(A, 0.02, A, A, 7, 16, A, ODD, None) == ALIGN
+    assert g(A, 0.02, A, A, 0, 16, A, None, None) == OK
 
 
 def test_gemm_small_and_gate_validation(tq):
@@ -252,6 +273,8 @@ def test_no_device_is_reported(tq):
     assert tq.lib.tq_pack(A, 8, 16, A, None) == DEVICE
     assert tq.lib.tq_ternarize(A, 8, 16, A, A, A, None) == DEVICE
     assert tq.lib.tq_rmsnorm_act_quant(A, 0, A, 1e-5, 1, 64, A, A, None) == DEVICE
+    assert tq.lib.tq_pack3(A, 7, 16, A, None) == DEVICE
+    assert tq.lib.tq_gemv3(A, 0.02, A, A, 7, 16, A, None, None) == DEVICE
     assert tq.lib.tq_rmsnorm_quant_gemv(A, 0, A, 1e-5, A, 0.02, 64, 64, A, None, A, A,
                                         None) == DEVICE
     assert tq.lib.tq_attn_decode(A, A, A, 20, 5, 128, 16, 0.1, A, A,
