@@ -38,6 +38,11 @@ namespace tq {
 tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
                   const int8_t *xq, const float *x_scale, int64_t N, int64_t K,
                   float *y, int32_t *acc0, int32_t *acc1, hipStream_t stream);
+// 2 <= M <= 4 on the vector ALU (tq_gemm_dot4.hip).
+bool gemm_dot4_fits(int64_t M, int64_t K);
+tq_status gemm_dot4(const uint8_t *p, float s_w, const int8_t *xq, const float *x_scale,
+                    int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
+                    int num_cus, hipStream_t stream);
 
 namespace {
 
@@ -345,6 +350,8 @@ tq_status gemm_small(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
     return gemv_m1(p0, s0, p1, s1, xq, x_scale, N, K, y, acc0, acc1, stream);
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
+  if (!p1 && gemm_dot4_fits(M, K))
+    return gemm_dot4(p0, s0, xq, x_scale, M, N, K, y, acc0, dev.num_cus, stream);
   GemmArgs a;
   a.p0 = p0;
   a.p1 = p1;

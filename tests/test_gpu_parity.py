@@ -232,10 +232,13 @@ def test_gate_up_relu2(env, M, N, K):
 
 
 # ------------------------------------------------------------------ gemm small
+# M <= 4 runs on the vector ALU (K <= 16384), larger M on the matrix cores
 GEMM_CASES = [(m, 6912, 2560) for m in (2, 4, 16, 64)] + \
-             [(m, 2560, 6912) for m in (4, 16, 64)] + \
+             [(m, 2560, 6912) for m in (2, 3, 4, 16, 64)] + \
              [(3, 20, 48), (5, 68, 80), (17, 260, 400), (33, 100, 1008),
-              (63, 64, 16), (48, 2052, 112)]
+              (63, 64, 16), (48, 2052, 112),
+              (2, 20, 16), (3, 52, 4112), (4, 100, 16384), (4, 64, 16400),
+              (2, 36, 1040), (4, 8, 32768)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
