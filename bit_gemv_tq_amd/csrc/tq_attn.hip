@@ -301,24 +301,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
 }
 
 // Block (h, slice): out[h, d] for kCombineDims dims d, merging the S <=
-// kAttnMaxSplits (one wave's width) chunk results of head h in fp64, all
-// loads issued at once:
+// kAttnMaxSplits chunk results of head h in fp64, all loads issued at once:
 //   M = max_c m_c,  den = sum_c e^(m_c - M) l_c,  out = sum_c e^(m_c - M) o_c / den
-// M and den: lane c of wave 0 holds chunk c, fixed butterfly trees (the
-// value of lane 0 is used).  Thread (sub, dd) sums the chunks c = sub,
-// sub + kCombineSubs, ... in order; the subranges are added in order.
+// M and den: thread c holds chunk c; fixed trees within each wave (every
+// lane ends with the same value), then the waves in order.  Thread
+// (sub, dd) sums the chunks c = sub, sub + kCombineSubs, ... in order; the
+// subranges are added in order.
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const float *__restrict__ part, int S, int D, float *__restrict__ out) {
-  static_assert(kAttnMaxSplits == kWave, "one chunk per lane of wave 0");
+  static_assert(kAttnMaxSplits <= kAttnThreads, "one chunk per thread");
   __shared__ double f[kAttnMaxSplits];  // e^(m_c - M)
-  __shared__ double den_s;
+  __shared__ double wred[2][kAttnNW];
   __shared__ double num_s[kCombineSubs][kCombineDims];
   const int h = blockIdx.x;
   const int dd = threadIdx.x % kCombineDims, sub = threadIdx.x / kCombineDims;
   const int d = blockIdx.y * kCombineDims + dd;
   const int RS = D + 4;
   const float *ph = part + (size_t)h * S * RS;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
   float mv = -INFINITY, lv = 0.0f;
   if (tid < S) {
@@ -331,18 +331,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const int c = sub + u * kCombineSubs;
     ov[u] = c < S ? ph[(size_t)c * RS + d] : 0.0f;
   }
-  if (tid < kWave) {
-    double M = (double)mv;
+  double M = (double)mv;
 #pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) M = fmax(M, __shfl_xor(M, off, kWave));
-    const double e = tid < S ? exp((double)mv - M) : 0.0;
-    f[tid] = e;
-    double den = e * (double)lv;
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
-    if (tid == 0) den_s = den;
-  }
+  for (int off = kWave / 2; off >= 1; off >>= 1) M = fmax(M, __shfl_xor(M, off, kWave));
+  if (lane == 0) wred[0][wave] = M;
   __syncthreads();
+  M = wred[0][0];
+#pragma unroll
+  for (int w = 1; w < kAttnNW; ++w) M = fmax(M, wred[0][w]);
+  const double e = tid < S ? exp((double)mv - M) : 0.0;
+  if (tid < kAttnMaxSplits) f[tid] = e;
+  double den = e * (double)lv;
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
+  if (lane == 0) wred[1][wave] = den;
+  __syncthreads();
+  den = wred[1][0];
+#pragma unroll
+  for (int w = 1; w < kAttnNW; ++w) den += wred[1][w];
   double num = 0.0;
 #pragma unroll
   for (int u = 0; u < kCombineBatch; ++u) {
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     double t = num_s[0][dd];
 #pragma unroll
     for (int q = 1; q < kCombineSubs; ++q) t += num_s[q][dd];
-    out[(size_t)h * D + d] = (float)(t / den_s);
+    out[(size_t)h * D + d] = (float)(t / den);
   }
 }
 
