@@ -43,7 +43,8 @@ constexpr int kAttnMinChunk = 64;    // smallest step of any (G, D, kT)
 constexpr int kAttnMaxSplits = 64;   // chunks per KV head
 constexpr int kCombineDims = 32;     // dims per combine block
 constexpr int kCombineSubs = kAttnThreads / kCombineDims;  // row subranges
-constexpr int kCombineBatch = kAttnMaxSplits / kCombineSubs;  // rows per thread
+constexpr int kCombineBatch =  // rows per thread
+    (kAttnMaxSplits + kCombineSubs - 1) / kCombineSubs;
 
 // Per (G, D, kT): lanes per token row, token slots, tokens per block step.
 // kT (tokens per lane slot and step) is at least LPT/G so that every lane
