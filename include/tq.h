@@ -151,7 +151,10 @@ TQ_API tq_status tq_gemv(const uint8_t *packed, float w_scale, const int8_t *xq,
 
 /*
  * tq_gemm_small -- the same product for a small batch of activation rows
- * (batched decode / short prefill), on the int8 matrix cores.
+ * (batched decode / short prefill), on the int8 matrix cores (M = 2, 3, and
+ * M = 4 with K >= 4096, on the vector ALU: the GEMV's structure with the
+ * rows in registers, which measured faster there).  Every row equals the
+ * M = 1 GEMV of that row bit for bit.
  *   xq       int8 [M,K] (16-B aligned), x_scale fp32 [M].
  *   y        fp32 [M,N], output: y[m,n] = (float)acc[m,n]*(s_w*x_scale[m]).
  *   acc      int32 [M,N], optional (NULL = skip).

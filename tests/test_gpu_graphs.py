@@ -103,3 +103,40 @@ def test_group_graph(env):
         torch.cuda.synchronize()
         for a, b in zip(ys, ref):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+
+
+def test_rmsnorm_gemv3_dot4_graph(env):
+    # one graph with the RMSNorm-fused GEMV, the five-per-byte GEMV and the
+    # vector-ALU small batch; every replay must equal the eager results
+    torch, tq = env
+    print("graph: rmsnorm_quant_gemv, gemv3, gemm_small M=3", flush=True)
+    N, K = 2560, 6912
+    codes = torch.from_numpy(workloads.ternary_codes(N, K, seed=81)).cuda()
+    p2, p3 = tq.tq_pack(codes), tq.tq_pack3(codes)
+    xb = workloads.activations_bf16(3, K, seed=82, outliers=True)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    gam = (1.0 + 0.2 * torch.randn(K, device="cuda")).to(torch.bfloat16)
+    xq, xs = tq.tq_act_quant(x)
+    torch.cuda.synchronize()
+    r1 = tq.tq_rmsnorm_quant_gemv(x[0], gam, p2, 0.02).clone()
+    r2 = tq.tq_gemv3(p3, 0.02, xq[0], xs[0:1], N).clone()
+    r3 = tq.tq_gemm_small(p2, 0.02, xq, xs).clone()
+    torch.cuda.synchronize()
+    y1, y2, y3 = torch.empty_like(r1), torch.empty_like(r2), torch.empty_like(r3)
+    q1 = torch.empty(K, dtype=torch.int8, device="cuda")
+    s1 = torch.empty(1, dtype=torch.float32, device="cuda")
+    xs0 = xs[0:1].clone()
+
+    def work():
+        tq.tq_rmsnorm_quant_gemv(x[0], gam, p2, 0.02, y=y1, xq=q1, x_scale=s1)
+        tq.tq_gemv3(p3, 0.02, xq[0], xs0, N, y2)
+        tq.tq_gemm_small(p2, 0.02, xq, xs, y3)
+    g = capture(torch, work)
+    for rep in range(4):
+        for t in (y1, y2, y3):
+            t.fill_(5.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in ((y1, r1), (y2, r2), (y3, r3)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
