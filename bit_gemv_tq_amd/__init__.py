@@ -211,7 +211,7 @@ def tq_gemv(packed, w_scale, xq, x_scale, y=None, acc=None, stream=None):
 
 def tq_gemm_small(packed, w_scale, xq, x_scale, y=None, acc=None, stream=None):
     """y[m,n] for a small batch xq [M, K] (M <= 64): int8 matrix cores, or
-    the vector ALU for M <= 4 where that measured faster."""
+    the vector ALU for M = 2 (K <= 16384), where that measured faster."""
     torch = _torch()
     _need(packed, "packed", torch.uint8)
     dev = packed.device

@@ -1,13 +1,13 @@
-// tq_gemm_dot4.hip -- the small-batch product for 2 <= M <= 4 activation rows
-// on the vector ALU (the M = 1 GEMV's structure with MR rows of x).
+// tq_gemm_dot4.hip -- the small-batch product for M = 2 activation rows on
+// the vector ALU (the M = 1 GEMV's structure with two rows of x).
 //
 // Page "Blog · field notes" (1bit engine), post "One GPU, many users": one
 // GPU serving several requests at once, i.e. a few activation rows per
-// weight read.  At M <= 4 the work per weight is small: the four plane masks
-// of a packed dword are shared by every row, and each row adds 4 v_dot4
-// (0.25 + 0.25 M operations per weight, 1.25 at M = 4), far below the VALU
-// rate at HBM speed, while the int8 matrix-core path pays operand expansion
-// and a cross-wave reduction for a 16-row tile that is three quarters empty.
+// weight read.  At M = 2 the work per weight is small: the four plane masks
+// of a packed dword are shared by both rows, and each row adds 4 v_dot4
+// (0.75 operations per weight), far below the VALU rate at HBM speed, while
+// the matrix-core kernel works on a 16-row activation tile that is seven
+// eighths empty.
 //
 // A team of LPR lanes owns one packed row (4 output rows per x row); lane l
 // reads pieces l + t*LPR (t < NP); its MR x NP activation pieces are loaded
@@ -203,14 +203,11 @@ tq_status launch_mr(const RegPlan &pl, const Dot4Args &a, hipStream_t s) {
 constexpr int kDot4MaxNP = 4;
 
 // Where this path is taken (measured on MI355X, pools of distinct weights):
-// M = 2, 3 always (M = 2: 3.9 / 4.1 us at [6912,2560] / [2560,6912]; the
-// matrix-core kernel works on a 16-row tile whatever M <= 16 and took 5.0 /
-// 6.1 us at M = 4); M = 4 only for rows of 4096 or more (5.3 vs 6.1 us at
-// [2560,6912], but 5.35 vs 5.0 us at [6912,2560], where the per-row
-// reduction of 16 sums is exposed behind short rows).
+// M = 2 (4.0 / 4.1 us at [6912,2560] / [2560,6912], against 4.1 / 4.7 us
+// for the matrix-core kernel); from M = 3 on the matrix-core kernel is
+// faster (4.1 / 4.7 us at M = 3 and 4, against 5.1 / 5.5 us here).
 bool gemm_dot4_fits(int64_t M, int64_t K) {
-  if (M < 2 || M > 4 || K < 16 || K / 16 > 256 * kDot4MaxNP) return false;
-  return M < 4 || K >= 4096;
+  return M == 2 && K >= 16 && K / 16 <= 256 * kDot4MaxNP;
 }
 
 // The narrowest team with at most 4 pieces per lane, 64-lane teams when rows
@@ -232,7 +229,7 @@ tq_status gemm_dot4(const uint8_t *p, float s_w, const int8_t *xq, const float *
   if (blocks > cap) blocks = cap;
   pl.blocks = (int)(blocks < 1 ? 1 : blocks);
   Dot4Args a{p, s_w, xq, x_scale, (int)M, (int)n4, (int)kp, y, acc};
-  return M == 2 ? launch_mr<2>(pl, a, stream) : launch_mr<4>(pl, a, stream);
+  return launch_mr<2>(pl, a, stream);
 }
 
 }  // namespace tq

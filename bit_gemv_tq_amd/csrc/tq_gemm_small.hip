@@ -9,27 +9,35 @@
 //
 // v_mfma_i32_16x16x64_i8 computes D[16x16] += A[16x64] * B[64x16]; lane l
 // supplies 16 bytes of A row l % 16 and of B column l % 16, both for the
-// same k block (l / 16), so the k order inside a step never matters.  A rows
-// are packed weight rows decoded to signed int8 {-1,0,+1} by one v_perm_b32
-// byte lookup per dword; B columns are activation rows.
+// same k block (l / 16), so which k a byte stands for is free as long as A
+// and B agree.  B columns are activation rows.
 //
-// Two kernel forms, both with one 16-row activation tile per block:
-//  * direct (M <= 16): a tile is TP = 4 or 8 packed rows; MFMA row r is
-//    packed row r / PL, plane r % PL + PL*h (PL = 16/TP planes per MFMA,
-//    4/PL MFMAs per load).  The lanes that share a packed piece load the
-//    same address, so a load touches only TP rows, and small TP gives enough
-//    tiles to spread the weight stream over every CU.
-//  * staged (M > 16): a tile is 16 packed rows (one plane per MFMA, four
-//    MFMAs per load) and M is split over blocks, so each block reads as
-//    many activation rows as weight rows.  Operands are loaded with
-//    contiguous 256-byte row segments (4 rows per load instruction), written
-//    to a wave-private LDS tile with a swizzle that keeps both the writes
-//    (one row, 16 pieces) and the MFMA-layout reads (16 rows, one piece)
-//    free of bank conflicts, then read back as MFMA operands.
-// In both forms the waves of a block own contiguous k ranges; their partial
-// tiles are summed in LDS with integer atomics (exact, order free).  Blocks
-// are mapped to tiles XCD-aware: the M-split blocks of one weight tile run
-// on one XCD, so all but the first read it from that XCD's L2.
+// Quad form.  MFMA row r = 4a + j is plane j of packed row a of a "quad" (4
+// packed rows = 16 output rows).  A wave works on 256-byte k groups (four
+// MFMA steps of 64).  Lane (kb, a, j) loads the 16 bytes of packed row a at
+// group offset 64j + 16kb, so one load instruction covers 4 rows x 256
+// contiguous bytes and every weight byte is loaded once.  For step u (group
+// offset 64u + 16kb) lane (kb, a, j) takes the dwords of lane (kb, a, u) of
+// its quad by a DPP quad broadcast folded into the AND that isolates its own
+// plane: one VALU operation per dword.  The planes are used as offset codes
+// c = w + 1 at scales 1, 4, 16 and, for plane 3, 64(c - 2) (bit 7 of every
+// byte is flipped once per load, so the masked byte stays a valid int8); a
+// fifth MFMA per step with A = all ones gives sum(x) per column, and
+//   sum(w x) = D0 - S = D1/4 - S = D2/16 - S = D3/64 + S   (exact shifts).
+// Activations are loaded 4 rows x 256 contiguous bytes per instruction and
+// written to a wave-private LDS tile with a swizzle (piece c of row m at
+// slot (c + m) mod 16) that makes both the writes and the MFMA-layout reads
+// free of bank conflicts.
+//
+// A block owns RG quads and one 16-row activation tile; its W waves split K
+// into groups (NQ per wave and pass, every load of a pass issued before the
+// first MFMA).  Per-wave partial tiles are summed in LDS (padded slots,
+// conflict free) and rescaled by RG * 64 threads.  Blocks map to tiles
+// XCD-aware: each XCD takes a contiguous run of tiles, the activation tiles
+// of one weight tile adjacent, so those share the weight tile in that XCD's
+// L2 and neighbouring tiles' partial output lines merge there.
+#include <algorithm>
+
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -38,7 +46,7 @@ namespace tq {
 tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
                   const int8_t *xq, const float *x_scale, int64_t N, int64_t K,
                   float *y, int32_t *acc0, int32_t *acc1, hipStream_t stream);
-// 2 <= M <= 4 on the vector ALU (tq_gemm_dot4.hip).
+// M = 2 on the vector ALU (tq_gemm_dot4.hip).
 bool gemm_dot4_fits(int64_t M, int64_t K);
 tq_status gemm_dot4(const uint8_t *p, float s_w, const int8_t *xq, const float *x_scale,
                     int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
@@ -48,7 +56,11 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kXcds = 8;  // MI355X: 8 XCDs, blocks dispatched round-robin
+constexpr int kXcds = 8;         // MI355X: 8 XCDs, blocks dispatched round-robin
+constexpr int kGroup = 256;      // k bytes per group (4 MFMA steps)
+constexpr int kTileSlots = 256;  // 16-byte slots of one 16-row x 256-byte tile
+constexpr int kSlotPad = 17;     // padded stride of the partial tiles
+constexpr int kLdsBytes = 160 * 1024;
 
 struct GemmArgs {
   const uint8_t *p0, *p1;
@@ -58,288 +70,307 @@ struct GemmArgs {
   int M, n4, K;
   float *y;
   int32_t *acc0, *acc1;
-  int ntiles, mtiles;  // weight tiles, 16-row activation tiles
+  int ntiles, mtiles;  // quad tiles, 16-row activation tiles
+  int per_xcd;         // blocks per XCD
 };
 
-// Block -> (weight tile, activation tile).  The grid is padded to a
-// multiple of kXcds * mtiles; block b runs on XCD b % kXcds, and the
-// mtiles consecutive blocks of one XCD share a weight tile.  Returns false
-// for padding blocks (the whole block exits before any barrier).
+// Block -> (weight tile, activation tile); false for padding blocks (the
+// whole block exits before any barrier).
 __device__ __forceinline__ bool block_tile(const GemmArgs &g, int &tile, int &mt) {
   const int b = blockIdx.x;
-  const int slot = b / kXcds;
-  tile = (slot / g.mtiles) * kXcds + b % kXcds;
-  mt = slot % g.mtiles;
+  const int t = (b % kXcds) * g.per_xcd + b / kXcds;
+  tile = t / g.mtiles;
+  mt = t % g.mtiles;
   return tile < g.ntiles;
 }
 
-// Signed weights of one plane of a 16-byte piece: codes {0,1,2} select the
-// bytes 0xFF, 0x00, 0x01 (-1, 0, +1) of a 4-byte table.  sh = 2 * plane.
-__device__ __forceinline__ v4i plane_operand(const u32x4 &w, int sh) {
-  constexpr uint32_t kTable = 0x000100FFu;
-  v4i a;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    a[d] = (int)__builtin_amdgcn_perm(0u, kTable, (w[d] >> sh) & 0x03030303u);
-  return a;
+// Lane U of each group of 4 lanes, to all 4 (DPP quad_perm [U,U,U,U]).
+template <int U>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  constexpr int ctrl = U | (U << 2) | (U << 4) | (U << 6);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ v4i as_v4i(const u32x4 &v) {
   return v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
 }
 
-// Rescale (and gate) one output (m, n) from its exact int32 sums.
-template <bool kGate>
-__device__ __forceinline__ void emit(const GemmArgs &g, int m, size_t n, int v0,
-                                     int v1) {
-  const size_t o = (size_t)m * g.n4 * 4 + n;
-  const float sx = g.x_scale[m];
-  if (g.acc0) g.acc0[o] = v0;
-  if constexpr (kGate) {
-    if (g.acc1) g.acc1[o] = v1;
-    g.y[o] = relu2_gate(rescale(v0, g.s0 * sx), rescale(v1, g.s1 * sx));
-  } else {
-    g.y[o] = rescale(v0, g.s0 * sx);
-  }
-}
-
-// ------------------------------------------------------------ direct form
-template <int TP, int U, int W, bool kGate>
-__global__ __launch_bounds__(W *kWave) void gemm_direct_kernel(GemmArgs g) {
-  constexpr int NM = kGate ? 2 : 1;
-  constexpr int PL = 16 / TP;  // planes per MFMA
-  constexpr int NG = 4 / PL;   // MFMAs per loaded piece
-  __shared__ int red[NM][NG][256];
-  int tile, mt;
-  if (!block_tile(g, tile, mt)) return;
-  for (int t = threadIdx.x; t < NM * NG * 256; t += W * kWave) (&red[0][0][0])[t] = 0;
-  __syncthreads();
-
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int r = lane & 15;  // MFMA row (A) / column (B) of this lane
-  const int i0 = tile * TP;
-  const int prow = min(i0 + r / PL, g.n4 - 1);  // past the end: reread
-  const int kb = 16 * (lane >> 4);
-  const int K = g.K;
-  const int nsteps = (K + 63) / 64;
-  const int per = (nsteps + W - 1) / W;
-  const int s0 = min(wave * per, nsteps), s1 = min(s0 + per, nsteps);
-  const uint8_t *P[NM];
-  P[0] = g.p0 + (size_t)prow * K;
-  if constexpr (kGate) P[NM - 1] = g.p1 + (size_t)prow * K;
-  const bool qok = r < g.M;  // one activation tile: M <= 16
-  const int8_t *Q = g.xq + (size_t)min(r, g.M - 1) * K;
-
-  v4i acc[NM][NG];
+// MFMA step U of group s: every quad of every matrix, then the ones column.
+template <int U, int NQ, int NM, int RG>
+__device__ __forceinline__ void quad_step(const u32x4 (&w)[NQ][NM][RG], int s, const v4i &b,
+                                          uint32_t mask, v4i (&acc)[NM][RG], v4i &ones) {
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int h = 0; h < NG; ++h) acc[m][h] = v4i{0, 0, 0, 0};
-
-  for (int s = s0; s < s1; s += U) {
-    // U k steps of loads in flight.  Slots past this wave's range (or past
-    // K: K % 64 may leave a ragged step) reread an in-bounds piece and get a
-    // zero activation operand.
-    u32x4 w[U][NM];
-    v4i b[U];
+    for (int q = 0; q < RG; ++q) {
+      v4i a;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = (s + u) * 64 + kb;
-      const bool ok = s + u < s1 && kk < K;
-      const int k = ok ? kk : 0;
+      for (int d = 0; d < 4; ++d) a[d] = (int)(quad_bcast<U>(w[s][m][q][d]) & mask);
+      acc[m][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[m][q], 0, 0, 0);
+    }
+  ones = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+      v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101}, b, ones, 0, 0, 0);
+}
+
+// Partial tiles: slot ((m RG + q) 4 + kb) kSlotPad + r, then the wave:
+// [slot][quad_wave_stride(W)].  The stride is odd, so 8 consecutive lanes
+// (one LDS cycle of 16-byte accesses) hit 8 bank groups on the writes (one
+// wave, consecutive r) and on the reads (consecutive slots of 17), and the
+// W partials of a slot are one address plus immediate offsets.
+__host__ __device__ constexpr int quad_wave_stride(int w) { return w | 1; }
+
+// LDS: [W][NQ][kTileSlots] activation tiles, then the partial tiles and
+// MAXW slots of slack (reads past the last wave).  blockDim.x = 64 W, W <=
+// MAXW.
+template <int RG, int NQ, bool kGate, int MAXW>
+__global__ __launch_bounds__(MAXW *kWave) void gemm_quad_kernel(GemmArgs g) {
+  constexpr int NM = kGate ? 2 : 1;
+  extern __shared__ u32x4 lds[];
+  int tile, mt;
+  if (!block_tile(g, tile, mt)) return;
+  const int W = blockDim.x / kWave;
+  __builtin_assume(W >= 1 && W <= MAXW);
+  const int PS = quad_wave_stride(W);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int kb = lane >> 4, r = lane & 15, j = r & 3;
+  const int K = g.K, n4 = g.n4, M = g.M;
+  const int m0 = mt * 16, i0 = tile * 4 * RG;
+  u32x4 *xt = lds + (size_t)wave * NQ * kTileSlots;
+  v4i *part = reinterpret_cast<v4i *>(lds + (size_t)W * NQ * kTileSlots);
+
+  const uint8_t *wr[NM][RG];  // this lane's packed row of each quad
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int q = 0; q < RG; ++q)
+      wr[m][q] = (m == 0 ? g.p0 : g.p1) + (size_t)min(i0 + 4 * q + (r >> 2), n4 - 1) * K;
+  // plane j of a flipped byte: c, 4c, 16c, or 64(c - 2) for plane 3
+  const uint32_t mask = j == 3 ? 0xC0C0C0C0u : (0x03030303u << (2 * j));
+
+  v4i acc[NM][RG], ones = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int q = 0; q < RG; ++q) acc[m][q] = v4i{0, 0, 0, 0};
+
+  const int groups = (K + kGroup - 1) / kGroup;
+  for (int g0 = wave * NQ; g0 < groups; g0 += W * NQ) {
+    // 1. Every load of the pass.  Past K (a ragged last group, or groups past
+    // the end) weights re-read offset 0 and activations are zeroed below.
+    u32x4 w[NQ][NM][RG], xv[NQ][4];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const int kw = (g0 + s) * kGroup + 64 * j + 16 * kb;
+      const int kc = kw < K ? kw : 0;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
-        w[u][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(P[m] + k));
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(Q + k);
-      b[u] = (ok && qok) ? as_v4i(v) : v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < RG; ++q)
+          w[s][m][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr[m][q] + kc));
     }
-    // Keep all U steps of loads ahead of the first MFMA.
+#pragma unroll
+    for (int s = 0; s < NQ; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + (lane >> 4);  // tile row; slot lane & 15 holds
+        const int k = (g0 + s) * kGroup + 16 * (((lane & 15) - row) & 15);
+        const int8_t *xr = g.xq + (size_t)min(m0 + row, M - 1) * K;
+        xv[s][i] = *reinterpret_cast<const u32x4 *>(xr + (k < K ? k : 0));
+      }
+    // Keep the loads ahead of the first MFMA.
     __builtin_amdgcn_sched_barrier(0);
+    // 2. Activation tiles to LDS (rows past M and k past K as zeros).
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int s = 0; s < NQ; ++s)
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int h = 0; h < NG; ++h)
-          acc[m][h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-              plane_operand(w[u][m], 2 * (r % PL + PL * h)), b[u], acc[m][h], 0, 0, 0);
-  }
-
-  // Exact cross-wave reduction, then the epilogue.  D element i of lane l is
-  // row rr = 4*(l/16) + i (packed row i0 + rr/PL, plane rr%PL + PL*h) of
-  // column l % 16 (activation row).
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int h = 0; h < NG; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(&red[m][h][lane * 4 + i], acc[m][h][i]);
-  __syncthreads();
-  for (int h = wave; h < NG; h += W) {
-    if (r >= g.M) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * (lane >> 4) + i;
-      const int p = i0 + rr / PL;
-      if (p >= g.n4) continue;
-      const size_t n = (size_t)(rr % PL + PL * h) * g.n4 + p;
-      emit<kGate>(g, r, n, red[0][h][lane * 4 + i], red[NM - 1][h][lane * 4 + i]);
-    }
-  }
-}
-
-// ------------------------------------------------------------ staged form
-constexpr int kStageJ = 16;              // 16-byte pieces per row per batch
-constexpr int kStageSlots = 16 * kStageJ;  // one 16-row operand tile
-
-// LDS slot of piece j (k = batch base + 16 j) of tile row r (0..15).  The
-// bank group of a slot is its index mod 16: (r + j) mod 16 differs across
-// the 16 rows of one piece (MFMA reads) and across 16 pieces of one row
-// (writes), so neither access conflicts.
-__device__ __forceinline__ int stage_slot(int r, int j) {
-  return (j >> 2) * 64 + (j & 3) * 16 + ((r + j) & 15);
-}
-
-template <int W, bool kGate>
-__global__ __launch_bounds__(W *kWave) void gemm_staged_kernel(GemmArgs g) {
-  constexpr int NM = kGate ? 2 : 1;
-  constexpr int RPI = kWave / kStageJ;  // rows per load instruction (4)
-  constexpr int NI = 16 / RPI;          // load instructions per operand tile
-  __shared__ u32x4 stage[W][(NM + 1) * kStageSlots];
-  __shared__ int red[NM][4][256];
-  int tile, mt;
-  if (!block_tile(g, tile, mt)) return;
-  for (int t = threadIdx.x; t < NM * 4 * 256; t += W * kWave) (&red[0][0][0])[t] = 0;
-
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  u32x4 *As = stage[wave];                      // NM weight tiles
-  u32x4 *Bs = stage[wave] + NM * kStageSlots;   // activation tile
-  const int i0 = tile * 16;
-  const int K = g.K;
-  const int m0 = mt * 16;
-  const int mvalid = min(g.M - m0, 16);
-  // Activation rows >= mvalid stay zero for the whole kernel.
-  for (int t = lane; t < kStageSlots; t += kWave) Bs[t] = u32x4{0, 0, 0, 0};
-  const int nb = (K + 16 * kStageJ - 1) / (16 * kStageJ);
-  const int per = (nb + W - 1) / W;
-  const int b0 = min(wave * per, nb), b1 = min(b0 + per, nb);
-  const int lrow = lane / kStageJ, lj = lane % kStageJ;  // load-side mapping
-  v4i acc[NM][4];
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = v4i{0, 0, 0, 0};
-  __syncthreads();
-
-  for (int bb = b0; bb < b1; ++bb) {
-    const int k = bb * 16 * kStageJ + 16 * lj;
-    const bool kok = k < K;
-    const int kc = kok ? k : K - 16;  // in bounds; its activation is zeroed
-    u32x4 wv[NM][NI], xv[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int prow = min(i0 + i * RPI + lrow, g.n4 - 1);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint8_t *p = (m == 0 ? g.p0 : g.p1) + (size_t)prow * K + kc;
-        wv[m][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + (lane >> 4);
+        const int k = (g0 + s) * kGroup + 16 * (((lane & 15) - row) & 15);
+        xt[s * kTileSlots + 64 * i + lane] =
+            (m0 + row < M && k < K) ? xv[s][i] : u32x4{0, 0, 0, 0};
       }
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = min(m0 + i * RPI + lrow, g.M - 1);
-      if (i * RPI < mvalid)  // uniform: some row of this load is valid
-        xv[i] = *reinterpret_cast<const u32x4 *>(g.xq + (size_t)row * K + kc);
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-        As[m * kStageSlots + stage_slot(i * RPI + lrow, lj)] = wv[m][i];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = i * RPI + lrow;
-      if (i * RPI < mvalid)
-        Bs[stage_slot(r, lj)] = (kok && r < mvalid) ? xv[i] : u32x4{0, 0, 0, 0};
-    }
-    // The tile is private to this wave, and a wave's LDS accesses complete
-    // in order; this only keeps the compiler from moving accesses across.
+    // The tile is private to this wave and a wave's LDS accesses complete in
+    // order; this keeps the compiler from moving accesses across.
     __builtin_amdgcn_wave_barrier();
+    // 3. Decode and multiply.
 #pragma unroll
-    for (int u = 0; u < kStageJ / 4; ++u) {
-      const int slot = stage_slot(lane & 15, 4 * u + (lane >> 4));
-      const v4i b = as_v4i(Bs[slot]);
+    for (int s = 0; s < NQ; ++s) {
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const u32x4 a = As[m * kStageSlots + slot];
+      for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(plane_operand(a, 2 * j), b,
-                                                            acc[m][j], 0, 0, 0);
-      }
+        for (int q = 0; q < RG; ++q)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) w[s][m][q][d] ^= 0x80808080u;
+      v4i b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        b[u] = as_v4i(xt[s * kTileSlots + 16 * r + ((4 * u + kb + r) & 15)]);
+      quad_step<0>(w, s, b[0], mask, acc, ones);
+      quad_step<1>(w, s, b[1], mask, acc, ones);
+      quad_step<2>(w, s, b[2], mask, acc, ones);
+      quad_step<3>(w, s, b[3], mask, acc, ones);
     }
     __builtin_amdgcn_wave_barrier();
   }
 
+  // 4. True sums of this wave's k range (D element i of lane l: plane i of
+  // packed row i0 + 4q + l/16, activation row m0 + l % 16).
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(&red[m][j][lane * 4 + i], acc[m][j][i]);
+    for (int q = 0; q < RG; ++q) {
+      v4i v = acc[m][q];
+      v[0] = v[0] - ones[0];
+      v[1] = (v[1] >> 2) - ones[1];
+      v[2] = (v[2] >> 4) - ones[2];
+      v[3] = (v[3] >> 6) + ones[3];
+      part[(((m * RG + q) * 4 + kb) * kSlotPad + r) * PS + wave] = v;
+    }
   __syncthreads();
-  // D element i of lane l: packed row i0 + 4*(l/16) + i of plane j, column
-  // (activation row m0 + l % 16).
-  const int mrow = m0 + (lane & 15);
-  for (int j = wave; j < 4; j += W) {
-    if (mrow >= g.M) continue;
+  // 5. Cross-wave sums (exact) and the epilogue.  Thread t: packed row
+  // i0 + 4q + aa, activation row m0 + mm; consecutive threads, consecutive
+  // output columns.  The scale is read once, before the stores (y may alias
+  // it).
+  const size_t N = (size_t)n4 * 4;
+  for (int t = threadIdx.x; t < RG * 64; t += blockDim.x) {
+    const int aa = t & 3, q = (t >> 2) % RG, mm = t / (4 * RG);
+    v4i v[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      v[m] = v4i{0, 0, 0, 0};
+      // 8 reads in flight at a time; those past W (the next slot or the
+      // slack) add nothing
+      const v4i *ps = part + (((m * RG + q) * 4 + aa) * kSlotPad + mm) * PS;
+#pragma unroll
+      for (int c = 0; c < MAXW; c += 8) {
+        v4i pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = ps[c + j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[m] += c + j < W ? pv[j] : v4i{0, 0, 0, 0};
+      }
+    }
+    const int p = i0 + 4 * q + aa, m = m0 + mm;
+    if (p >= n4 || m >= M) continue;
+    const float sx = g.x_scale[m];
+    const float c0 = g.s0 * sx, c1 = g.s1 * sx;
+    const size_t o = (size_t)m * N + p;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = i0 + 4 * (lane >> 4) + i;
-      if (p >= g.n4) continue;
-      emit<kGate>(g, mrow, (size_t)j * g.n4 + p, red[0][j][lane * 4 + i],
-                  red[NM - 1][j][lane * 4 + i]);
+      const size_t oi = o + (size_t)i * n4;
+      if (g.acc0) g.acc0[oi] = v[0][i];
+      if constexpr (kGate) {
+        if (g.acc1) g.acc1[oi] = v[NM - 1][i];
+        g.y[oi] = relu2_gate(rescale(v[0][i], c0), rescale(v[NM - 1][i], c1));
+      } else {
+        g.y[oi] = rescale(v[0][i], c0);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------ launch
-// Grid: tiles padded so every XCD gets whole groups of mtiles blocks.
-dim3 gemm_grid(const GemmArgs &a) {
-  const int groups = (a.ntiles + kXcds - 1) / kXcds;
-  return dim3((unsigned)(groups * kXcds * a.mtiles));
+struct QuadPlan {
+  int rg, nq, w;
+};
+
+// Largest NQ whose kernel stays within the register budget of its launch
+// bound without spilling: 128 VGPRs for blocks of up to 16 waves, 256 for up
+// to 8 (the compiler's gfx950 register counts of every RG x NQ x form; 0:
+// no NQ fits; the gated form's epilogue alone needs more than 128).
+constexpr int quad_max_nq(int nm, int rg, int maxw) {
+  if (maxw > 8) return nm == 1 ? (rg == 1 ? 3 : rg == 2 ? 2 : rg == 4 ? 1 : 0) : 0;
+  return nm == 1 ? (rg <= 4 ? 4 : 3) : (rg <= 2 ? 4 : 3);
+}
+
+constexpr int quad_lds(int rg, int nq, int nm, int w) {
+  return w * nq * kTileSlots * 16 +
+         (nm * rg * 4 * kSlotPad * quad_wave_stride(w) + (w > 8 ? 16 : 8)) * 16;
+}
+
+// Quads per block: the largest RG that still gives about 5/8 of a block per
+// CU (measured on MI355X: a larger RG re-reads less of the activation tile,
+// too few blocks leave CUs idle).  Groups per wave and pass: the fewest
+// passes over K with at most 16 waves, within the register table above and
+// the LDS, ties to the smaller NQ.
+QuadPlan plan_quad(int64_t M, int64_t n4, int64_t K, bool gate, int num_cus, int &mtiles) {
+  const int nm = gate ? 2 : 1;
+  mtiles = (int)((M + 15) / 16);
+  QuadPlan pl{1, 1, 1};
+  for (int rg : {8, 4, 2}) {
+    if (rg * nm > 8) continue;
+    if ((n4 + 4 * rg - 1) / (4 * rg) * mtiles >= (5 * num_cus) / 8) {
+      pl.rg = rg;
+      break;
+    }
+  }
+  auto fits = [&](int nq, int w) {
+    return nq <= quad_max_nq(nm, pl.rg, w > 8 ? 16 : 8) &&
+           quad_lds(pl.rg, nq, nm, w) <= kLdsBytes;
+  };
+  const int64_t groups = (K + kGroup - 1) / kGroup;
+  int64_t best = INT64_MAX;
+  for (int nq = 1; nq <= 4; ++nq) {
+    int w = (int)std::min<int64_t>(16, std::max<int64_t>(1, (groups + nq - 1) / nq));
+    while (w > 1 && !fits(nq, w)) --w;
+    if (!fits(nq, w)) continue;
+    const int64_t passes = (groups + (int64_t)w * nq - 1) / ((int64_t)w * nq);
+    if (passes < best) {
+      best = passes;
+      pl.nq = nq;
+      pl.w = w;
+    }
+  }
+  return pl;
+}
+
+template <int RG, int NQ, bool kGate, int MAXW>
+tq_status launch_quad(const QuadPlan &pl, const GemmArgs &a, dim3 grid, hipStream_t s) {
+  if constexpr (NQ > quad_max_nq(kGate ? 2 : 1, RG, MAXW)) {
+    return TQ_ERR_LAUNCH;  // never planned
+  } else {
+    auto k = gemm_quad_kernel<RG, NQ, kGate, MAXW>;
+    const int bytes = quad_lds(RG, NQ, kGate ? 2 : 1, pl.w);
+    if (tq_status e = allow_dynamic_lds(reinterpret_cast<const void *>(k), bytes)) return e;
+    return launch(k, grid, dim3(pl.w * kWave), bytes, s, a);
+  }
+}
+
+template <int RG, int NQ, bool kGate>
+tq_status launch_quad_w(const QuadPlan &pl, const GemmArgs &a, dim3 grid, hipStream_t s) {
+  return pl.w <= 8 ? launch_quad<RG, NQ, kGate, 8>(pl, a, grid, s)
+                   : launch_quad<RG, NQ, kGate, 16>(pl, a, grid, s);
+}
+
+template <int RG, bool kGate>
+tq_status launch_quad_nq(const QuadPlan &pl, const GemmArgs &a, dim3 grid, hipStream_t s) {
+  switch (pl.nq) {
+    case 1: return launch_quad_w<RG, 1, kGate>(pl, a, grid, s);
+    case 2: return launch_quad_w<RG, 2, kGate>(pl, a, grid, s);
+    case 3: return launch_quad_w<RG, 3, kGate>(pl, a, grid, s);
+    case 4: return launch_quad_w<RG, 4, kGate>(pl, a, grid, s);
+  }
+  return TQ_ERR_LAUNCH;
 }
 
 template <bool kGate>
 tq_status launch_gemm(GemmArgs a, int num_cus, hipStream_t s) {
-  if (a.M <= 16) {
-    // Direct form.  Tile height: 8 packed rows while that still gives about
-    // one tile per CU (measured: taller tiles cut activation re-reads),
-    // else 4 so the weight stream is spread over every CU.
-    a.mtiles = 1;
-    if ((int64_t)a.n4 >= 8LL * num_cus * 3 / 4) {
-      a.ntiles = (a.n4 + 7) / 8;
-      return launch(gemm_direct_kernel<8, 4, 16, kGate>, gemm_grid(a),
-                    dim3(16 * kWave), 0, s, a);
-    }
-    a.ntiles = (a.n4 + 3) / 4;
-    if constexpr (kGate)
-      return launch(gemm_direct_kernel<4, 4, 8, kGate>, gemm_grid(a),
-                    dim3(8 * kWave), 0, s, a);
-    else
-      return launch(gemm_direct_kernel<4, 8, 8, kGate>, gemm_grid(a),
-                    dim3(8 * kWave), 0, s, a);
+  const QuadPlan pl = plan_quad(a.M, a.n4, a.K, kGate, num_cus, a.mtiles);
+  a.ntiles = (a.n4 + 4 * pl.rg - 1) / (4 * pl.rg);
+  // Blocks per XCD: a whole number of activation tiles per weight tile.
+  int per = (a.ntiles * a.mtiles + kXcds - 1) / kXcds;
+  per = (per + a.mtiles - 1) / a.mtiles * a.mtiles;
+  a.per_xcd = per;
+  const dim3 grid((unsigned)(per * kXcds));
+  switch (pl.rg) {
+    case 1: return launch_quad_nq<1, kGate>(pl, a, grid, s);
+    case 2: return launch_quad_nq<2, kGate>(pl, a, grid, s);
+    case 4: return launch_quad_nq<4, kGate>(pl, a, grid, s);
+    case 8:
+      if constexpr (!kGate) return launch_quad_nq<8, kGate>(pl, a, grid, s);
+      break;
   }
-  // Staged form, M split into 16-row blocks.  About two 256-byte k batches
-  // per wave (16 waves for long rows); the gated form holds two weight
-  // tiles per wave, so it stays at 8 waves (LDS).
-  a.mtiles = (a.M + 15) / 16;
-  a.ntiles = (a.n4 + 15) / 16;
-  const int nb = (a.K + 255) / 256;
-  if (!kGate && nb >= 20)
-    return launch(gemm_staged_kernel<16, false>, gemm_grid(a), dim3(16 * kWave), 0,
-                  s, a);
-  return launch(gemm_staged_kernel<8, kGate>, gemm_grid(a), dim3(8 * kWave), 0, s, a);
+  return TQ_ERR_LAUNCH;
 }
 
 tq_status gemm_small(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
@@ -365,7 +396,7 @@ tq_status gemm_small(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
   a.y = y;
   a.acc0 = acc0;
   a.acc1 = acc1;
-  a.ntiles = a.mtiles = 0;  // set by the launcher
+  a.ntiles = a.mtiles = a.per_xcd = 0;  // set by the launcher
   return p1 ? launch_gemm<true>(a, dev.num_cus, stream)
             : launch_gemm<false>(a, dev.num_cus, stream);
 }

@@ -15,6 +15,12 @@
  *            near the memory-bandwidth peak is the decode hot loop).
  *   [DIGEST] "BitNet" news-digest tag page, first item: weights in {-1,0,1}
  *            replace multiplies with adds and subtracts.
+ *   [README] "1bit.systems" project README -- sections "hardware" and
+ *            "honest numbers".
+ *   [BLOG]   "Blog · field notes" (1bit engine) -- posts "Qwen3.8-27B at
+ *            45.7 tok/s" (decode is bandwidth bound, prompt processing
+ *            matrix-unit bound) and "One GPU, many users" (several requests
+ *            served by one GPU).
  *
  * Data conventions (shared by every call):
  *   - W is an [N,K] matrix of ternary weights w in {-1,0,+1}.  Packed form:
@@ -151,10 +157,10 @@ TQ_API tq_status tq_gemv(const uint8_t *packed, float w_scale, const int8_t *xq,
 
 /*
  * tq_gemm_small -- the same product for a small batch of activation rows
- * (batched decode / short prefill), on the int8 matrix cores (M = 2, 3, and
- * M = 4 with K >= 4096, on the vector ALU: the GEMV's structure with the
- * rows in registers, which measured faster there).  Every row equals the
- * M = 1 GEMV of that row bit for bit.
+ * (batched decode / short prefill; [BLOG] "One GPU, many users"), on the
+ * int8 matrix cores (M = 2 with K <= 16384 on the vector ALU instead: the
+ * GEMV's structure with both rows in registers, which measured faster
+ * there).  Every row equals the M = 1 GEMV of that row bit for bit.
  *   xq       int8 [M,K] (16-B aligned), x_scale fp32 [M].
  *   y        fp32 [M,N], output: y[m,n] = (float)acc[m,n]*(s_w*x_scale[m]).
  *   acc      int32 [M,N], optional (NULL = skip).

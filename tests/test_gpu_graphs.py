@@ -109,7 +109,7 @@ def test_rmsnorm_gemv3_dot4_graph(env):
     # one graph with the RMSNorm-fused GEMV, the five-per-byte GEMV and the
     # vector-ALU small batch; every replay must equal the eager results
     torch, tq = env
-    print("graph: rmsnorm_quant_gemv, gemv3, gemm_small M=3", flush=True)
+    print("graph: rmsnorm_quant_gemv, gemv3, gemm_small M=2", flush=True)
     N, K = 2560, 6912
     codes = torch.from_numpy(workloads.ternary_codes(N, K, seed=81)).cuda()
     p2, p3 = tq.tq_pack(codes), tq.tq_pack3(codes)
@@ -120,7 +120,8 @@ def test_rmsnorm_gemv3_dot4_graph(env):
     torch.cuda.synchronize()
     r1 = tq.tq_rmsnorm_quant_gemv(x[0], gam, p2, 0.02).clone()
     r2 = tq.tq_gemv3(p3, 0.02, xq[0], xs[0:1], N).clone()
-    r3 = tq.tq_gemm_small(p2, 0.02, xq, xs).clone()
+    q2, s2 = xq[:2].contiguous(), xs[:2].contiguous()
+    r3 = tq.tq_gemm_small(p2, 0.02, q2, s2).clone()
     torch.cuda.synchronize()
     y1, y2, y3 = torch.empty_like(r1), torch.empty_like(r2), torch.empty_like(r3)
     q1 = torch.empty(K, dtype=torch.int8, device="cuda")
@@ -130,7 +131,7 @@ def test_rmsnorm_gemv3_dot4_graph(env):
     def work():
         tq.tq_rmsnorm_quant_gemv(x[0], gam, p2, 0.02, y=y1, xq=q1, x_scale=s1)
         tq.tq_gemv3(p3, 0.02, xq[0], xs0, N, y2)
-        tq.tq_gemm_small(p2, 0.02, xq, xs, y3)
+        tq.tq_gemm_small(p2, 0.02, q2, s2, y3)
     g = capture(torch, work)
     for rep in range(4):
         for t in (y1, y2, y3):
@@ -139,4 +140,44 @@ def test_rmsnorm_gemv3_dot4_graph(env):
         g.replay()
         torch.cuda.synchronize()
         for a, b in ((y1, r1), (y2, r2), (y3, r3)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+
+
+def test_gemm_quad_graph(env):
+    # the matrix-core small batch in one graph: M = 16 and 64, two shapes, the
+    # gated form at M = 32 (dynamic LDS above 64 KB, one and two blocks of
+    # partial tiles per wave); every replay must equal the eager results
+    torch, tq = env
+    print("graph: gemm_small M=16, 64; gate_up M=32", flush=True)
+    cases = [(16, 6912, 2560), (64, 2560, 6912)]
+    ps, qs, ss, refs = [], [], [], []
+    for i, (M, N, K) in enumerate(cases):
+        ps.append(tq.tq_pack(torch.from_numpy(workloads.ternary_codes(N, K, seed=91 + i)).cuda()))
+        xb = workloads.activations_bf16(M, K, seed=93 + i, outliers=True)
+        q, s = tq.tq_act_quant(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda())
+        qs.append(q)
+        ss.append(s)
+    pg = tq.tq_pack(torch.from_numpy(workloads.ternary_codes(6912, 2560, seed=95)).cuda())
+    pu = tq.tq_pack(torch.from_numpy(workloads.ternary_codes(6912, 2560, seed=96)).cuda())
+    xb = workloads.activations_bf16(32, 2560, seed=97, outliers=True)
+    qg, sg = tq.tq_act_quant(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    for p, q, s in zip(ps, qs, ss):
+        refs.append(tq.tq_gemm_small(p, 0.02, q, s).clone())
+    refs.append(tq.tq_gate_up_relu2(pg, 0.024, pu, 0.025, qg, sg).clone())
+    torch.cuda.synchronize()
+    ys = [torch.empty_like(r) for r in refs]
+
+    def work():
+        for p, q, s, y in zip(ps, qs, ss, ys):
+            tq.tq_gemm_small(p, 0.02, q, s, y)
+        tq.tq_gate_up_relu2(pg, 0.024, pu, 0.025, qg, sg, ys[-1])
+    g = capture(torch, work)
+    for rep in range(4):
+        for t in ys:
+            t.fill_(5.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ys, refs):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep

@@ -207,7 +207,8 @@ def test_gemv_zero_k_and_empty(env):
 @pytest.mark.parametrize("M,N,K", [(1, 6912, 2560), (1, 20, 48), (1, 100, 1008),
                                    (1, 256, 28672), (1, 8, 40000), (1, 1028, 4608),
                                    (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560),
-                                   (16, 2052, 112), (33, 260, 400), (64, 2560, 6912)])
+                                   (16, 2052, 112), (33, 260, 400), (64, 2560, 6912),
+                                   (32, 6912, 2560), (32, 2560, 6912), (8, 516, 20000)])
 def test_gate_up_relu2(env, M, N, K):
     torch, tq, oracle = env
     say(f"gate_up M={M} N={N} K={K}")
@@ -232,13 +233,17 @@ def test_gate_up_relu2(env, M, N, K):
 
 
 # ------------------------------------------------------------------ gemm small
-# M <= 4 runs on the vector ALU (K <= 16384), larger M on the matrix cores
-GEMM_CASES = [(m, 6912, 2560) for m in (2, 4, 16, 64)] + \
-             [(m, 2560, 6912) for m in (2, 3, 4, 16, 64)] + \
+# M = 2 runs on the vector ALU (K <= 16384), M >= 3 on the matrix cores.
+# The matrix-core plans these shapes take (quads per block RG, groups per wave
+# NQ, waves W, passes over K): every RG in {1, 2, 4, 8}, NQ 1..4, W 1..16,
+# blocks of up to 8 and up to 16 waves, one to four passes, ragged K (not a
+# multiple of 256) and ragged N (not a multiple of 16 RG).
+GEMM_CASES = [(m, 6912, 2560) for m in (2, 3, 4, 8, 16, 32, 64)] + \
+             [(m, 2560, 6912) for m in (2, 3, 4, 16, 32, 64)] + \
              [(3, 20, 48), (5, 68, 80), (17, 260, 400), (33, 100, 1008),
               (63, 64, 16), (48, 2052, 112),
               (2, 20, 16), (3, 52, 4112), (4, 100, 16384), (4, 64, 16400),
-              (2, 36, 1040), (4, 8, 32768)]
+              (2, 36, 1040), (4, 8, 32768), (16, 512, 28672), (2, 12, 20000)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
