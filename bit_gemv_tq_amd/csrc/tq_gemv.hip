@@ -194,8 +194,7 @@ tq_status launch_gemv_lds(const GemvPlan &pl, const GemvArgs &a, size_t lds,
 // 3 per CU (2 for the two-stream gate kernel).  Grids that give every team
 // exactly the same number of rows measured slower (all waves reach their
 // reductions at once), so the grid is not trimmed to a balanced count.
-RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate,
-                      bool rms = false) {
+RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate, int xt) {
   RegPlan pl{};
   int lpr = 16;
   while ((kp + lpr - 1) / lpr > 8) lpr *= 2;
@@ -204,13 +203,16 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate,
   pl.lpr = lpr;
   pl.np = (int)((kp + lpr - 1) / lpr);
   pl.exact = (int64_t)pl.np * lpr == kp;
-  const int bt = reg_block_threads(lpr);
+  const int bt = gemv_block_threads(lpr, xt);
   const int64_t teams = bt / lpr;
   int64_t blocks = (n4 + teams - 1) / teams;
-  // Resident blocks per CU (persistent grid): 8-12 waves per CU, measured
-  // best on MI355X; the two-plane gate kernel and the RMSNorm prologue hold
-  // more registers (one 512-thread block per CU is what fits).
-  const int per_cu = bt == 512 ? (gate || rms ? 1 : 2) : (gate ? 2 : 3);
+  // Resident blocks per CU (persistent grid): 12 waves per CU, measured best
+  // on MI355X (at [8192,28672], 256-lane teams: 3 one-team blocks per CU
+  // took 12.7 / 11.1 us with the bf16 / int8 row against 13.5 / 11.4 us for
+  // 2 two-team blocks and 14.2 / 12.3 us for 4 one-team blocks); the
+  // two-plane gate kernel holds more registers, 2 per CU; the 512-thread
+  // fp32 and RMSNorm forms 2 and 1 (what their registers allow).
+  const int per_cu = bt == 512 ? (gate || xt_rms(xt) ? 1 : 2) : (gate ? 2 : 3);
   const int64_t cap = (int64_t)num_cus * per_cu;
   if (blocks > cap) blocks = cap;
   pl.blocks = (int)(blocks < 1 ? 1 : blocks);
@@ -240,7 +242,7 @@ tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
   if (kp >= 1 && kp <= kRegMaxPieces) {
     RegArgs a{p0,  p1,   s0,   s1,      xq,      x_scale, (int)n4, (int)kp,
               y,   acc0, acc1, nullptr, nullptr, nullptr, nullptr};
-    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate), gate,
+    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate, kXInt8), gate,
                            kXInt8, a, stream);
   }
   // K == 0 or K > 32768: activations read from LDS per piece.
@@ -276,8 +278,9 @@ tq_status quant_gemv_m1(const void *x, tq_dtype xt, const uint8_t *p0,
   if (N > 0 && kp >= 1 && kp <= kRegMaxPieces) {
     RegArgs a{p0, p1,   s0,   s1, nullptr, nullptr, (int)n4, (int)kp,
               y,  acc0, acc1, x,  xq,      x_scale, y_scale};
-    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate), gate,
-                           xt == TQ_BF16 ? kXBf16 : kXF32, a, stream);
+    const int form = xt == TQ_BF16 ? kXBf16 : kXF32;
+    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, gate, form), gate, form,
+                           a, stream);
   }
   if (tq_status s = tq_act_quant(x, xt, 1, K, xq, x_scale, stream)) return s;
   if (N == 0) return TQ_OK;
@@ -298,8 +301,9 @@ tq_status rmsnorm_quant_gemv_m1(const void *x, tq_dtype xt, const void *gamma,
               y,  acc0,    nullptr, x, xq,      x_scale, nullptr};
     a.gamma = gamma;
     a.eps = eps;
-    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, false, true), false,
-                           xt == TQ_BF16 ? kXBf16Rms : kXF32Rms, a, stream);
+    const int form = xt == TQ_BF16 ? kXBf16Rms : kXF32Rms;
+    return launch_gemv_reg(plan_gemv_reg(n4, kp, dev.num_cus, false, form), false, form,
+                           a, stream);
   }
   if (tq_status s = rmsnorm_act_quant(x, xt, gamma, eps, 1, K, xq, x_scale, stream))
     return s;
@@ -356,8 +360,9 @@ tq_status quant_gemv_group(const void *x, tq_dtype xt, int count,
     a.y_scale = y_scale;
     a.p0 = a.seg.p[0];  // unused by the grouped form; kept valid
     a.y = a.seg.y[0];
-    return launch_gemv_reg(plan_gemv_reg(total, kp, dev.num_cus, false), false,
-                           xt == TQ_BF16 ? kXBf16 : kXF32, a, stream);
+    const int form = xt == TQ_BF16 ? kXBf16 : kXF32;
+    return launch_gemv_reg(plan_gemv_reg(total, kp, dev.num_cus, false, form), false,
+                           form, a, stream);
   }
   if (tq_status s = tq_act_quant(x, xt, 1, K, xq, x_scale, stream)) return s;
   for (int i = 0; i < count; ++i) {

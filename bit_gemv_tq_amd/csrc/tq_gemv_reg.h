@@ -11,7 +11,9 @@
 // row at a time (4 output rows, one per plane).  Lane l of a team always
 // reads the 16-byte pieces l + t*LPR (t < NP) of a row, so the int8
 // activation pieces it needs are the same for every row: they are staged
-// once per block through LDS and then held in VGPRs.  The hot loop is NP
+// once per block through LDS (a 256-lane team, alone in its block, loads
+// exactly its own pieces and skips LDS) and then held in VGPRs.  Blocks
+// have 256 threads.  The hot loop is NP
 // non-temporal 16-byte weight loads per lane and row plus 16 v_dot4 per
 // piece (tq_device.h), with no LDS traffic.  Each lane starts its plane
 // accumulators at -scale_j * sum(its activation bytes), so after the team
@@ -30,9 +32,8 @@ namespace tq {
 
 constexpr int kRegThreads = 256;
 
-// Block size per team width: 256-lane teams (K > 16384) run two teams per
-// 512-thread block, so the two share one staged (and, for raw rows,
-// quantized) activation row; narrower teams use 256-thread blocks.
+// Block size of the five-per-byte GEMV and the M = 2 vector kernel, which
+// share the team structure: 256-lane teams run two to a 512-thread block.
 constexpr int reg_block_threads(int lpr) { return lpr >= 256 ? 512 : kRegThreads; }
 constexpr int kRegMaxPieces = 2048;  // K <= 32768 bytes
 
@@ -43,6 +44,14 @@ constexpr int kRegMaxPieces = 2048;  // K <= 32768 bytes
 constexpr int kXInt8 = 0, kXBf16 = 1, kXF32 = 2, kXBf16Rms = 3, kXF32Rms = 4;
 constexpr bool xt_rms(int xt) { return xt == kXBf16Rms || xt == kXF32Rms; }
 constexpr bool xt_bf16(int xt) { return xt == kXBf16 || xt == kXBf16Rms; }
+
+// Block size of the GEMV: 256 threads, one 256-lane team or several
+// narrower ones.  The fp32 and RMSNorm prologues of a 256-lane team hold
+// too many registers for one team per block (up to 400 VGPRs), so those run
+// two teams per 512-thread block, sharing the staged row.
+constexpr int gemv_block_threads(int lpr, int xt) {
+  return lpr >= 256 && (xt == kXF32 || xt_rms(xt)) ? 512 : kRegThreads;
+}
 
 // Grouped form: several weight matrices with the same K that read one
 // activation row (e.g. the q, k and v projections), run as one packed-row
@@ -107,11 +116,15 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   constexpr int WPT = LPR > kWave ? LPR / kWave : 1;  // waves per team
   constexpr int SPAN = NP * LPR;                      // pieces a team covers
   constexpr int SP = (SPAN + BT - 1) / BT;  // staging loads
+  // One team per block (256-lane teams): thread i stages pieces i + s*BT,
+  // which are exactly its own pieces lane + t*LPR (SP == NP), so the row
+  // needs no LDS round trip and no barrier between staging and use.
+  constexpr bool kOwn = G == 1;
   static_assert(NP >= 1 && SPAN <= kRegMaxPieces, "pieces per lane");
   constexpr int VPP = XT == kXInt8 ? 1 : (xt_bf16(XT) ? 2 : 4);  // words/piece
   constexpr bool kRms = xt_rms(XT);
   constexpr int GPP = kRms ? VPP : 1;  // gamma words per piece (unused: 1)
-  __shared__ u32x4 x_lds[SP * BT];  // padded: stores unconditional
+  __shared__ u32x4 x_lds[kOwn ? 1 : SP * BT];  // padded: stores unconditional
   __shared__ int red[2][BT / kWave][NM][4];
   __shared__ float amax_lds[BT / kWave];
   __shared__ double ss_lds[kRms ? BT / kWave : 1];
@@ -177,11 +190,16 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. Stage x through LDS (quantizing a raw row first); keep this lane's
-  // pieces in VGPRs.
+  // pieces in VGPRs.  With one team per block the staged pieces stay in
+  // the thread's registers (own[]).
   float sx;
+  u32x4 own[kOwn ? SP : 1];
   if constexpr (XT == kXInt8) {
 #pragma unroll
-    for (int s = 0; s < SP; ++s) x_lds[threadIdx.x + s * BT] = xs[s][0];
+    for (int s = 0; s < SP; ++s) {
+      if constexpr (kOwn) own[s] = xs[s][0];
+      else x_lds[threadIdx.x + s * BT] = xs[s][0];
+    }
     sx = g.x_scale[0];
   } else {
     // Per-token absmax over the whole row (every block, redundantly), then
@@ -244,20 +262,23 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
     for (int s = 0; s < SP; ++s) {
       const int p = (int)threadIdx.x + s * BT;
       const u32x4 q = quant_piece<kQBf16>(qv[s], inv);
-      x_lds[threadIdx.x + s * BT] = q;
+      if constexpr (kOwn) own[s] = q;
+      else x_lds[threadIdx.x + s * BT] = q;
       if (writer && p < kp)
         reinterpret_cast<u32x4 *>(g.xq_out)[p] = q;
     }
     if (writer && threadIdx.x == 0) g.xs_out[0] = s_x;
     sx = g.y_scale ? g.y_scale[0] : s_x;
   }
-  __syncthreads();
+  if constexpr (!kOwn) __syncthreads();
   uint4 xr[NP];
   int sq = 0;
 #pragma unroll
   for (int t = 0; t < NP; ++t) {
     const int p = lane + t * LPR;
-    const u32x4 v = x_lds[p];
+    u32x4 v;
+    if constexpr (kOwn) v = own[t];
+    else v = x_lds[p];
     xr[t] = (EXACT || p < kp) ? make_uint4(v[0], v[1], v[2], v[3])
                               : make_uint4(0, 0, 0, 0);
     sq = sum_bytes16(xr[t], sq);
@@ -357,10 +378,11 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
                      hipStream_t s);
 
 #define TQ_REG_KERNEL(LPR, NPV, GATE, XT)                                      \
-  (pl.exact ? gemv_reg_kernel<LPR, NPV, true, GATE, XT, reg_block_threads(LPR)> \
-            : gemv_reg_kernel<LPR, NPV, false, GATE, XT, reg_block_threads(LPR)>)
+  (pl.exact ? gemv_reg_kernel<LPR, NPV, true, GATE, XT, gemv_block_threads(LPR, XT)>  \
+            : gemv_reg_kernel<LPR, NPV, false, GATE, XT, gemv_block_threads(LPR, XT)>)
 
 #define TQ_REG_NP_CASES(LPR, GATE, XT)                                         \
+  const dim3 block(gemv_block_threads(LPR, XT));                               \
   switch (pl.np) {                                                             \
     case 1: return launch(TQ_REG_KERNEL(LPR, 1, GATE, XT), grid, block, 0, s, a); \
     case 2: return launch(TQ_REG_KERNEL(LPR, 2, GATE, XT), grid, block, 0, s, a); \
@@ -396,7 +418,7 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
   template <>                                                                  \
   tq_status launch_reg_part<LPR, GATE>(const RegPlan &pl, int xt,              \
                                        const RegArgs &a, hipStream_t s) {      \
-    const dim3 grid(pl.blocks), block(reg_block_threads(LPR));                 \
+    const dim3 grid(pl.blocks);                                                \
     TQ_REG_XT_CASES(LPR, GATE)                                                 \
   }
 
@@ -404,7 +426,7 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
   template <>                                                                  \
   tq_status launch_reg_part<LPR, false>(const RegPlan &pl, int xt,             \
                                         const RegArgs &a, hipStream_t s) {     \
-    const dim3 grid(pl.blocks), block(reg_block_threads(LPR));                 \
+    const dim3 grid(pl.blocks);                                                \
     TQ_REG_XT_CASES_RMS(LPR)                                                   \
   }
 
