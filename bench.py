@@ -262,6 +262,9 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="only run a 256 MiB calibration copy and the dominant "
                          "kernel (for rocprofv3 --pmc runs), then exit")
+    ap.add_argument("--counters-gemm", action="store_true",
+                    help="only run the small-batch GEMM at each benchmarked "
+                         "(M, N, K), 8 launches each (for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -281,6 +284,9 @@ def main():
 
     if args.counters:
         counters_run(torch, tq, workloads, dev)
+        return
+    if args.counters_gemm:
+        gemm_counters_run(torch, tq, workloads, dev)
         return
 
     # ---------------------------------------------------------------- pools
@@ -458,6 +464,37 @@ def counters_run(torch, tq, workloads, dev):
         tq.tq_quant_gemv(xt, P[r % 4], 0.02, yy, xq=q, x_scale=s)
     torch.cuda.synchronize()
     log("counters run done")
+
+
+def gemm_counters_run(torch, tq, workloads, dev):
+    """Dispatches for the small-batch GEMM counters (MFMA operations and
+    busy cycles, fetched bytes): a 256 MiB calibration copy, then for each
+    benchmarked shape and M, 8 launches over 4 distinct weight copies."""
+    import numpy as np
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for (N, K) in workloads.GEMM_SMALL_SHAPES:
+        P = []
+        for c in range(4):
+            w = workloads.ternary_codes_torch(N, K, seed=5252 + c, device=dev)
+            P.append(tq.tq_pack(w))
+            del w
+        for M in workloads.GEMM_SMALL_M:
+            xb = workloads.activations_bf16(M, K, seed=95 + M)
+            xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev).reshape(M, K)
+            q, s = tq.tq_act_quant(xt)
+            yy = torch.empty(M, N, dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            log(f"gemm counters M={M} N={N} K={K}")
+            for r in range(8):
+                tq.tq_gemm_small(P[r % 4], 0.02, q, s, yy)
+            torch.cuda.synchronize()
+        del P
+    log("gemm counters run done")
 
 
 def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
