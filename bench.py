@@ -23,7 +23,9 @@ Timing:
     launch (packed weights + bf16 x + int8 x written + fp32 scale + fp32 y)
     / time per launch, against 8 TB/s.  Back-to-back time includes the short gap
     between graph nodes, so it is an upper bound on the kernel duration
-    that rocprofv3's kernel trace reports.
+    that rocprofv3's kernel trace reports.  Beside it, the measured read
+    ceiling: tq_stream_read (the same 16-byte non-temporal loads and nothing
+    else) over the same pool, and the kernel's fraction of it.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
     gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64), the absmean
     ternarizer, split-KV decode attention and the 30-layer decode-step chain
@@ -386,6 +388,24 @@ def main():
     dom_us = per_shape[DOMINANT]["quant_gemv"]["us_per_launch"]
     achieved = algo_bytes_fused(dN, dK) / dom_us / 1e3
 
+    # the measured read ceiling: a read-only kernel (tq_stream_read, the
+    # GEMV's 16-byte non-temporal access and nothing else) over the same pool
+    sink = torch.zeros(4096, 4, dtype=torch.int32, device=dev)
+
+    def read_loop(start):
+        P = pools[DOMINANT]
+        for r in range(R):
+            tq.tq_stream_read(P[(start + r) % len(P)], sink)
+    nP = len(pools[DOMINANT])
+    gs = [timer.graph(lambda s=s: read_loop(s)) for s in range(0, nP, max(1, nP // 4))][:4]
+    read_us = timer.time_graphs(gs, 8) * 1e3 / R
+    del gs
+    read_gbs = weight_bytes(dN, dK) / read_us / 1e3
+    ceiling = {"us_per_launch": round(read_us, 3), "GBs": round(read_gbs, 1),
+               "pct_hbm_peak": round(100 * read_gbs / HBM_PEAK_GBS, 1),
+               "bytes": weight_bytes(dN, dK)}
+    log(f"read ceiling over the {DOMINANT} pool: {ceiling}")
+
     rows = {}
     if not args.no_rows:
         rows = measure_rows(torch, tq, workloads, timer, dev, R, per_shape)
@@ -418,6 +438,7 @@ def main():
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
             "unfused_ms_per_step": round(ms_step_u, 5),
+            "read_ceiling": ceiling,
         },
         "roofline": {
             "bound": "hbm",
@@ -429,6 +450,8 @@ def main():
             "traffic": read_traffic(),
             "us_per_launch": dom_us,
             "bytes_per_launch": algo_bytes_fused(dN, dK),
+            "read_ceiling_GBs": round(read_gbs, 1),
+            "frac_of_read_ceiling": round(achieved / read_gbs, 4),
         },
         "per_shape": per_shape,
         "rows": rows,

@@ -31,7 +31,7 @@ EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
            "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
            "tq_quant_gemv_group", "tq_ternarize", "tq_attn_decode",
            "tq_rmsnorm_act_quant", "tq_rmsnorm_quant_gemv", "tq_pack3", "tq_gemv3",
-           "tq_status_string")
+           "tq_stream_read", "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "tq_rmsnorm_act_quant": [p, i32, p, f32, i64, i64, p, p, p],
         "tq_pack3": [p, i64, i64, p, p],
         "tq_gemv3": [p, f32, p, p, i64, i64, p, p, p],
+        "tq_stream_read": [p, i64, p, i64, p],
         "tq_rmsnorm_quant_gemv": [p, i32, p, f32, p, f32, i64, i64, p, p, p, p, p],
     }
     for name, args in sigs.items():
@@ -168,6 +169,28 @@ def tq_gemv3(packed, w_scale, xq, x_scale, N, y=None, acc=None, stream=None):
                                     _ptr(x_scale), N, K, _ptr(y), _ptr(acc),
                                     _stream(stream)))
     return y
+
+
+def tq_stream_read(buf, sink=None, stream=None):
+    """Read the whole contiguous device tensor `buf` (byte size a multiple
+    of 16) with the GEMV's access pattern and nothing else (the measured read
+    ceiling).  Returns `sink`, uint32 [words, 4]: block b's word is the XOR
+    of the 16-byte words it read (unused words are zeroed when the sink is
+    allocated here)."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda":
+        raise ValueError("buf must be a GPU tensor")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros(4096, 4, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32, buf.device)
+    if sink.dim() != 2 or sink.shape[1] != 4:
+        raise ValueError("sink must be int32 [words, 4]")
+    _check("tq_stream_read", lib.tq_stream_read(_ptr(buf), nbytes, _ptr(sink),
+                                                sink.shape[0], _stream(stream)))
+    return sink
 
 
 def tq_act_quant(x, xq=None, x_scale=None, stream=None):

@@ -343,6 +343,25 @@ TQ_API tq_status tq_attn_decode(const float *q, const void *k_cache,
                                 hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
+/*
+ * tq_stream_read -- measurement helper: the practical HBM read ceiling that
+ * the GEMV's weight stream is compared with ([ARC] TL;DR and [README]
+ * "hardware": a GEMV is judged by the fraction of memory bandwidth it
+ * reaches).  Reads `bytes` of `buf` with the GEMV's access (16-byte
+ * non-temporal loads, consecutive lanes on consecutive pieces) and does
+ * nothing else.
+ *   buf         device, 16-B aligned; bytes % 16 == 0 (bytes == 0: no-op).
+ *   sink        device, 16-B aligned, `sink_words` 16-byte words.  Block b
+ *               writes word b: the XOR of the 16-byte words it read, so the
+ *               XOR of the written words equals the XOR of every 16-byte
+ *               word of buf; at most min(sink_words, 4 x CUs) words are
+ *               written, the rest are left as they were.
+ * Errors: TQ_ERR_SHAPE (bytes < 0, bytes % 16, sink_words < 1), TQ_ERR_NULL,
+ * TQ_ERR_ALIGN, TQ_ERR_DEVICE, TQ_ERR_LAUNCH.
+ */
+TQ_API tq_status tq_stream_read(const void *buf, int64_t bytes, void *sink,
+                                int64_t sink_words, hipStream_t stream);
+
 TQ_API const char *tq_status_string(tq_status status);
 
 #ifdef __cplusplus

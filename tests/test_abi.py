@@ -35,7 +35,7 @@ def test_header_declares_the_calls():
                           "tq_quant_gate_up_relu2", "tq_quant_gemv_group",
                           "tq_ternarize", "tq_attn_decode", "tq_rmsnorm_act_quant",
                           "tq_rmsnorm_quant_gemv", "tq_pack3", "tq_gemv3",
-                          "tq_status_string"}
+                          "tq_stream_read", "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -266,6 +266,19 @@ def _no_gpu():
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="checks the no-device path")
+def test_stream_read_validation(tq):
+    f = tq.lib.tq_stream_read
+    #        buf  bytes sink words stream
+    assert f(A, 24, A, 8, None) == SHAPE       # bytes % 16
+    assert f(A, -16, A, 8, None) == SHAPE
+    assert f(A, 64, A, 0, None) == SHAPE       # sink_words >= 1
+    assert f(None, 64, A, 8, None) == NULL
+    assert f(A, 64, None, 8, None) == NULL
+    assert f(MIS, 64, A, 8, None) == ALIGN
+    assert f(A, 64, MIS, 8, None) == ALIGN
+    assert f(A, 0, A, 8, None) == OK           # empty: no-op
+
+
 def test_no_device_is_reported(tq):
     # Valid arguments on a machine with no GPU: TQ_ERR_DEVICE, nothing runs.
     assert gemv(tq) == DEVICE
@@ -275,6 +288,7 @@ def test_no_device_is_reported(tq):
     assert tq.lib.tq_rmsnorm_act_quant(A, 0, A, 1e-5, 1, 64, A, A, None) == DEVICE
     assert tq.lib.tq_pack3(A, 7, 16, A, None) == DEVICE
     assert tq.lib.tq_gemv3(A, 0.02, A, A, 7, 16, A, None, None) == DEVICE
+    assert tq.lib.tq_stream_read(A, 64, A, 8, None) == DEVICE
     assert tq.lib.tq_rmsnorm_quant_gemv(A, 0, A, 1e-5, A, 0.02, 64, 64, A, None, A, A,
                                         None) == DEVICE
     assert tq.lib.tq_attn_decode(A, A, A, 20, 5, 128, 16, 0.1, A, A,
