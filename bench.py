@@ -41,6 +41,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -82,11 +83,22 @@ def algo_bytes_fused(N, K):
     return N * K // 4 + 2 * K + K + 4 + 4 * N
 
 
-def kernel_source_hash():
+def code_only(text):
+    """Source text without // comments and blank lines: a comment edit does
+    not change the kernel the counters were taken on."""
+    lines = (re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines())
+    return "\n".join(l for l in lines if l)
+
+
+def kernel_source_hash(read=None):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(code_only(text).encode())
     return h.hexdigest()[:16]
 
 

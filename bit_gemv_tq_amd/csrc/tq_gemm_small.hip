@@ -172,7 +172,8 @@ __global__ __launch_bounds__(MAXW *kWave) void gemm_quad_kernel(GemmArgs g) {
     for (int s = 0; s < NQ; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 4 * i + (lane >> 4);  // tile row; slot lane & 15 holds
+        // tile row `row`, slot lane & 15: piece (slot - row) mod 16 of the group
+        const int row = 4 * i + (lane >> 4);
         const int k = (g0 + s) * kGroup + 16 * (((lane & 15) - row) & 15);
         const int8_t *xr = g.xq + (size_t)min(m0 + row, M - 1) * K;
         xv[s][i] = *reinterpret_cast<const u32x4 *>(xr + (k < K ? k : 0));

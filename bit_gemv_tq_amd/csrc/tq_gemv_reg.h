@@ -13,7 +13,8 @@
 // activation pieces it needs are the same for every row: they are staged
 // once per block through LDS (a 256-lane team, alone in its block, loads
 // exactly its own pieces and skips LDS) and then held in VGPRs.  Blocks
-// have 256 threads.  The hot loop is NP
+// have 256 threads (512, two teams, for the fp32 and RMSNorm forms of
+// 256-lane teams).  The hot loop is NP
 // non-temporal 16-byte weight loads per lane and row plus 16 v_dot4 per
 // piece (tq_device.h), with no LDS traffic.  Each lane starts its plane
 // accumulators at -scale_j * sum(its activation bytes), so after the team
