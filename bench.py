@@ -17,7 +17,10 @@ Timing:
     the 256 MB Infinity Cache cannot serve repeats; step i uses copy i mod C.
   * Steps and kernel loops are captured in HIP graphs; a spin kernel queued
     before the start event keeps the host ahead, so HIP events on the
-    launch stream measure GPU execution only.
+    launch stream measure GPU execution only.  A step graph holds 12
+    consecutive steps (one pass over the copies), so the fixed cost of a
+    graph replay (about 5 us) is spread as in a decode graph of a layer
+    stack; the time with one step per graph is reported too.
   * roofline: the dominant kernel (the fused [8192, 28672] launch) is timed
     as a graph of back-to-back launches over its pool; algorithmic bytes per
     launch (packed weights + bf16 x + int8 x written + fp32 scale + fp32 y)
@@ -245,6 +248,24 @@ class Timer:
         torch.cuda.synchronize()
         return g
 
+    def time_steps(self, multi, singles, steps):
+        """ms per step for exactly `steps` steps: `multi` holds len(singles)
+        consecutive steps, replayed steps // S times, then the remainder as
+        one-step graphs."""
+        torch = self.torch
+        S = len(singles)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN)
+        e0.record()
+        for _ in range(steps // S):
+            multi.replay()
+        for i in range(steps % S):
+            singles[i].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     def time_graphs(self, graphs, reps):
         """ms per replay, cycling through `graphs` for `reps` replays."""
         torch = self.torch
@@ -336,22 +357,42 @@ def main():
             tq.tq_act_quant(x[name], xq[name], xs[name])
             tq.tq_gemv(pools[name][i % STEP_COPIES], s_w, xq[name], xs[name], y[name])
 
+    def steps_of(fn):
+        # STEP_COPIES consecutive steps, one pass over the weight copies
+        def run():
+            for i in range(STEP_COPIES):
+                fn(i)
+        return run
+
     # ---------------------------------------------------------------- step
+    # One graph holds STEP_COPIES consecutive steps (3 * STEP_COPIES kernel
+    # nodes, as a decode graph holds a whole layer stack): each graph replay
+    # has a fixed launch cost of about 5 us on this part, which a graph of
+    # one 3-kernel step would charge to every step.  The one-step-per-graph
+    # time is reported beside it.
     log("capturing step graphs")
-    graphs = [timer.graph(lambda i=i: step(i)) for i in range(STEP_COPIES)]
-    for i in range(args.warmup):
-        graphs[i % STEP_COPIES].replay()
+    singles = [timer.graph(lambda i=i: step(i)) for i in range(STEP_COPIES)]
+    multi = timer.graph(steps_of(step))
+    for _ in range(args.warmup // STEP_COPIES):
+        multi.replay()
+    for i in range(args.warmup % STEP_COPIES):
+        singles[i].replay()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ms_step = timer.time_graphs(graphs, args.steps)
+    ms_step = timer.time_steps(multi, singles, args.steps)
     wall = time.perf_counter() - wall0
     step_wbytes = sum(weight_bytes(*s) for s in SHAPES.values())
     value = step_wbytes / (ms_step * 1e-3) / 1e9
     log(f"step: {ms_step * 1e3:.2f} us -> {value:.0f} GB/s")
-    graphs_u = [timer.graph(lambda i=i: step_unfused(i)) for i in range(STEP_COPIES)]
-    ms_step_u = timer.time_graphs(graphs_u, args.steps)
+    ms_step_1 = timer.time_graphs(singles, args.steps)
+    log(f"step, one step per graph: {ms_step_1 * 1e3:.2f} us")
+    del singles, multi
+    singles_u = [timer.graph(lambda i=i: step_unfused(i)) for i in range(STEP_COPIES)]
+    multi_u = timer.graph(steps_of(step_unfused))
+    multi_u.replay()
+    ms_step_u = timer.time_steps(multi_u, singles_u, args.steps)
     log(f"unfused step (act_quant + gemv launches): {ms_step_u * 1e3:.2f} us")
-    del graphs_u
+    del singles_u, multi_u
 
     # ------------------------------------------------- per-kernel loops
     R = args.kernel_reps
@@ -449,6 +490,8 @@ def main():
             "pool_copies_per_shape": {k: len(v) for k, v in pools.items()},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "steps_per_graph": STEP_COPIES,
+            "ms_per_step_one_step_per_graph": round(ms_step_1, 5),
             "unfused_ms_per_step": round(ms_step_u, 5),
             "read_ceiling": ceiling,
         },

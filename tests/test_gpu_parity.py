@@ -208,7 +208,8 @@ def test_gemv_zero_k_and_empty(env):
                                    (1, 256, 28672), (1, 8, 40000), (1, 1028, 4608),
                                    (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560),
                                    (16, 2052, 112), (33, 260, 400), (64, 2560, 6912),
-                                   (32, 6912, 2560), (32, 2560, 6912), (8, 516, 20000)])
+                                   (32, 6912, 2560), (32, 2560, 6912), (8, 516, 20000),
+                                   (2, 100, 1008), (3, 12, 131072)])
 def test_gate_up_relu2(env, M, N, K):
     torch, tq, oracle = env
     say(f"gate_up M={M} N={N} K={K}")
@@ -243,7 +244,8 @@ GEMM_CASES = [(m, 6912, 2560) for m in (2, 3, 4, 8, 16, 32, 64)] + \
              [(3, 20, 48), (5, 68, 80), (17, 260, 400), (33, 100, 1008),
               (63, 64, 16), (48, 2052, 112),
               (2, 20, 16), (3, 52, 4112), (4, 100, 16384), (4, 64, 16400),
-              (2, 36, 1040), (4, 8, 32768), (16, 512, 28672), (2, 12, 20000)]
+              (2, 36, 1040), (4, 8, 32768), (16, 512, 28672), (2, 12, 20000),
+              (2, 36, 12288), (3, 8, 131072)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
