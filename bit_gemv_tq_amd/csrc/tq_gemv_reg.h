@@ -109,6 +109,25 @@ __device__ __forceinline__ T seg_pick(const T (&v)[kMaxSeg], int q) {
   return r;
 }
 
+// Segment q's packed matrix, for the weight loads.  The candidates pass
+// through an empty asm statement that pins them in scalar registers: left
+// alone, the compiler folds the selects into an indexed vector load of the
+// argument block, whose wait (vmcnt 0) would also wait for every activation
+// load issued before it, so no weight load could start before the whole
+// activation row had arrived.  The result is marked as a global-memory
+// address again, so the weight loads stay global (not flat) loads.
+typedef __attribute__((address_space(1))) const uint8_t gbyte;
+__device__ __forceinline__ const uint8_t *seg_matrix(const RegSegs &sg, int q) {
+  uint64_t r = reinterpret_cast<uint64_t>(sg.p[0]);
+#pragma unroll
+  for (int t = 1; t < kMaxSeg; ++t) {
+    uint64_t v = reinterpret_cast<uint64_t>(sg.p[t]);
+    asm volatile("" : "+s"(v));
+    r = q == t ? v : r;
+  }
+  return (const uint8_t *)reinterpret_cast<gbyte *>(r);
+}
+
 template <int LPR, int NP, bool EXACT, bool kGate, int XT, int BT = kRegThreads>
 __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   constexpr int NM = kGate ? 2 : 1;
@@ -179,7 +198,7 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
       if (!kGate && g.seg.n > 0) {  // grouped: the row's own matrix
         int start;
         const int q = seg_of(g.seg, row, start);
-        rp = reinterpret_cast<const uint4 *>(seg_pick(g.seg.p, q)) +
+        rp = reinterpret_cast<const uint4 *>(seg_matrix(g.seg, q)) +
              (size_t)(row - start) * kp;
       }
 #pragma unroll
