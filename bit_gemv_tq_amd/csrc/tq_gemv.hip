@@ -216,11 +216,32 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate, int xt) {
   const int64_t cap = (int64_t)num_cus * per_cu;
   if (blocks > cap) blocks = cap;
   pl.blocks = (int)(blocks < 1 ? 1 : blocks);
+  // Rows by dispatch round, for one-team blocks that quantize a bf16 row in
+  // the prologue.  The dispatcher places blocks breadth first (block b on a
+  // CU in round b / CUs), and on MI355X the second and third block of a CU
+  // receive their activation row 2.4 and 4.5 us after the first, behind that
+  // block's weight misses (per-block timestamps at [8192,28672]).  Rows are
+  // therefore split 4 : 3 : 1 between the rounds instead of evenly: 13.2-13.3
+  // against 13.5-13.6 us per back-to-back launch there.  Only where every
+  // block of every round gets a row (n4 >= 8 per CU) and the grid is exactly
+  // three rounds.  (The int8 row arrives early enough in every round: a
+  // split by round measured 0.3 us slower for tq_gemv.)  Which block takes
+  // which row does not change any result.
+  if (lpr == 256 && bt == kRegThreads && xt == kXBf16 && !gate &&
+      pl.blocks == 3 * num_cus && n4 >= 8 * (int64_t)num_cus) {
+    pl.round_cus = num_cus;
+    pl.round_end0 = (int)(n4 * 4 / 8);
+    pl.round_end1 = (int)(n4 * 7 / 8);
+  }
   return pl;
 }
 
 tq_status launch_gemv_reg(const RegPlan &pl, bool gate, int xt,
-                          const RegArgs &a, hipStream_t s) {
+                          const RegArgs &args, hipStream_t s) {
+  RegArgs a = args;
+  a.round_cus = pl.round_cus;
+  a.round_end0 = pl.round_end0;
+  a.round_end1 = pl.round_end1;
   switch (pl.lpr) {
     case 16: return launch_reg<16>(pl, gate, xt, a, s);
     case 32: return launch_reg<32>(pl, gate, xt, a, s);

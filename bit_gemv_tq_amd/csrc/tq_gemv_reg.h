@@ -86,6 +86,10 @@ struct RegArgs {
   RegSegs seg;           // grouped form (not with kGate); n4 = total rows
   const void *gamma;     // [K] RMSNorm weights, dtype of x (kX*Rms)
   float eps;             // RMSNorm epsilon (kX*Rms)
+  // Rows by dispatch round (one-team blocks; 0 = off): block b is in round
+  // b / round_cus and walks the rows [0, end0), [end0, end1) or [end1, n4)
+  // of its round, strided by round_cus.  Set by the launcher from the plan.
+  int round_cus, round_end0, round_end1;
 };
 
 // Segment of global packed row i (grouped form): its first row and index.
@@ -153,9 +157,20 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
   const int lane = threadIdx.x % LPR;
   const int team = threadIdx.x / LPR;
   const int wave = threadIdx.x / kWave;
-  const int row_stride = gridDim.x * G;
-  const int rb0 = blockIdx.x * G;  // < n4 for every launched block
-  const int its = (n4 - 1 - rb0) / row_stride + 1;
+  int row_stride = gridDim.x * G;
+  int rb0 = blockIdx.x * G;  // < n4 for every launched block
+  int its;
+  if (kOwn && g.round_cus > 0) {
+    const int rnd = blockIdx.x / g.round_cus;
+    const int start = rnd == 0 ? 0 : (rnd == 1 ? g.round_end0 : g.round_end1);
+    const int end = rnd == 0 ? g.round_end0 : (rnd == 1 ? g.round_end1 : n4);
+    row_stride = g.round_cus;
+    rb0 = start + (int)blockIdx.x % g.round_cus;
+    if (rb0 >= end) return;  // the whole block, before any barrier
+    its = (end - 1 - rb0) / row_stride + 1;
+  } else {
+    its = (n4 - 1 - rb0) / row_stride + 1;
+  }
 
   const uint4 *P[NM];
   P[0] = reinterpret_cast<const uint4 *>(g.p0);
@@ -391,6 +406,7 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
 struct RegPlan {
   int lpr, np, blocks;
   bool exact;
+  int round_cus, round_end0, round_end1;  // rows by dispatch round (0: off)
 };
 
 template <int LPR>

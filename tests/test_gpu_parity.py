@@ -283,9 +283,12 @@ def test_gemm_small_zero_k(env):
 
 
 # ------------------------------------------------------------------ fused
+# (8192, 28672) and (8400, 20000) take the rows-by-dispatch-round mapping of
+# the bf16 form on a 256-CU part (the second: rounds of unequal row counts,
+# pieces past the row end).
 FUSED_SHAPES = [(4, 16), (12, 48), (100, 1008), (36, 2064), (2560, 2560),
                 (6912, 2560), (2560, 6912), (8, 32768), (4, 32784), (28, 16384),
-                (28672, 8192), (8192, 28672)]
+                (28672, 8192), (8192, 28672), (8400, 20000)]
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)
@@ -327,7 +330,8 @@ GROUP_CASES = [((2560, 640, 640), 2560, "bf16"),      # 2B-4T q, k, v
                ((8, 12, 4, 16), 28672, "bf16"),       # 256-lane teams
                ((4, 8), 40000, "f32"),                # K > 32768: fallback
                ((12, 4), 0, "bf16"),                  # K == 0
-               ((1024,), 4608, "bf16")]
+               ((1024,), 4608, "bf16"),
+               ((4096, 2048, 2048), 20480, "bf16")]  # rows by dispatch round
 
 
 @pytest.mark.parametrize("Ns,K,dtype", GROUP_CASES)
