@@ -95,6 +95,19 @@ __device__ __forceinline__ void widen8(const u32x4 &r, float (&x)[8]) {
   }
 }
 
+// The partner of a halving step at bit OFF, read through DPP (no LDS round
+// trip): within aligned groups of 2*OFF lanes, lane i takes lane 2*OFF-1-i
+// for OFF = 8 and 4 (row mirror, half-row mirror) and lane i ^ OFF for
+// OFF = 2 and 1 (quad permutations).  Each partner differs from i in bit
+// OFF and agrees with it in the bits above, which is all a step needs: both
+// then hold sums over the same lanes, of opposite halves.
+template <int OFF>
+__device__ __forceinline__ float butterfly_partner(float v) {
+  static_assert(OFF == 8 || OFF == 4 || OFF == 2 || OFF == 1, "step");
+  constexpr int ctrl = OFF == 8 ? 0x140 : (OFF == 4 ? 0x141 : (OFF == 2 ? 0x4e : 0xb1));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, false));
+}
+
 // One halving step of the reduce-scatter (and the steps after it), with
 // compile-time offsets and widths so every register index is a constant:
 // lanes whose bit OFF is set keep the upper half of their first W values,
@@ -107,7 +120,7 @@ __device__ __forceinline__ void reduce_scatter(float (&val)[N], int lt) {
     for (int k = 0; k < W / 2; ++k) {
       const float send = upper ? val[k] : val[k + W / 2];
       const float keep = upper ? val[k + W / 2] : val[k];
-      val[k] = keep + __shfl_xor(send, OFF, kWave);
+      val[k] = keep + butterfly_partner<OFF>(send);
     }
     reduce_scatter<OFF / 2, W / 2>(val, lt);
   }
