@@ -335,18 +335,52 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
   }
 }
 
+// Wave reductions by DPP that end in the last lane (row shifts within each
+// 16-lane row, then the two row broadcasts).  For the maximum a lane with no
+// source keeps its own value; for the sum it adds zero.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_keep(float v) {
+  const int x = __float_as_int(v);
+  return __int_as_float(__builtin_amdgcn_update_dpp(x, x, Ctrl, RowMask, 0xf, false));
+}
+
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ double dpp_zero(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, Ctrl, RowMask, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), Ctrl, RowMask, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+__device__ __forceinline__ float wave_max_last(float v) {
+  v = fmaxf(v, dpp_keep<0x111, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x112, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x114, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x118, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  return fmaxf(v, dpp_keep<0x143, 0xc>(v));
+}
+
+__device__ __forceinline__ double wave_sum_last(double v) {
+  v += dpp_zero<0x111, 0xf>(v);
+  v += dpp_zero<0x112, 0xf>(v);
+  v += dpp_zero<0x114, 0xf>(v);
+  v += dpp_zero<0x118, 0xf>(v);
+  v += dpp_zero<0x142, 0xa>(v);
+  return v + dpp_zero<0x143, 0xc>(v);
+}
+
 // Block (h, slice): out[h, d] for kCombineDims dims d, merging the S <=
 // kAttnMaxSplits chunk results of head h in fp64, all loads issued at once:
 //   M = max_c m_c,  den = sum_c e^(m_c - M) l_c,  out = sum_c e^(m_c - M) o_c / den
-// M and den: thread c holds chunk c; fixed trees within each wave (every
-// lane ends with the same value), then the waves in order.  Thread
-// (sub, dd) sums the chunks c = sub, sub + kCombineSubs, ... in order; the
-// subranges are added in order.
+// M and den: thread c of wave 0 holds chunk c; fixed DPP trees over that
+// wave, ending in its last lane.  Thread (sub, dd) sums the chunks c = sub,
+// sub + kCombineSubs, ... in order; the subranges are added in order.
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const float *__restrict__ part, int S, int D, float *__restrict__ out) {
   static_assert(kAttnMaxSplits <= kAttnThreads, "one chunk per thread");
   __shared__ double f[kAttnMaxSplits];  // e^(m_c - M)
-  __shared__ double wred[2][kAttnNW];
+  __shared__ double den_s;
   __shared__ double num_s[kCombineSubs][kCombineDims];
   const int h = blockIdx.x;
   const int dd = threadIdx.x % kCombineDims, sub = threadIdx.x / kCombineDims;
@@ -366,24 +400,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
     const int c = sub + u * kCombineSubs;
     ov[u] = c < S ? ph[(size_t)c * RS + d] : 0.0f;
   }
-  double M = (double)mv;
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) M = fmax(M, __shfl_xor(M, off, kWave));
-  if (lane == 0) wred[0][wave] = M;
+  // Every chunk is in wave 0 (S <= 64): its lanes form M and the
+  // denominator with DPP trees that end in the last lane; the weights e and
+  // the denominator reach the other waves through LDS.
+  if (wave == 0) {
+    const double M = __shfl((double)wave_max_last(mv), kWave - 1, kWave);
+    const double e = tid < S ? exp((double)mv - M) : 0.0;
+    f[tid] = e;
+    const double dsum = wave_sum_last(e * (double)lv);
+    if (lane == kWave - 1) den_s = dsum;
+  }
   __syncthreads();
-  M = wred[0][0];
-#pragma unroll
-  for (int w = 1; w < kAttnNW; ++w) M = fmax(M, wred[0][w]);
-  const double e = tid < S ? exp((double)mv - M) : 0.0;
-  if (tid < kAttnMaxSplits) f[tid] = e;
-  double den = e * (double)lv;
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
-  if (lane == 0) wred[1][wave] = den;
-  __syncthreads();
-  den = wred[1][0];
-#pragma unroll
-  for (int w = 1; w < kAttnNW; ++w) den += wred[1][w];
+  const double den = den_s;
   double num = 0.0;
 #pragma unroll
   for (int u = 0; u < kCombineBatch; ++u) {
