@@ -31,7 +31,7 @@ EXPORTS = ("tq_pack", "tq_act_quant", "tq_gemv", "tq_gemm_small",
            "tq_gate_up_relu2", "tq_quant_gemv", "tq_quant_gate_up_relu2",
            "tq_quant_gemv_group", "tq_ternarize", "tq_attn_decode",
            "tq_rmsnorm_act_quant", "tq_rmsnorm_quant_gemv", "tq_pack3", "tq_gemv3",
-           "tq_stream_read", "tq_status_string")
+           "tq_stream_read", "tq_attn_decode_noalloc", "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "tq_quant_gemv_group": [p, i32, i32, p, p, p, i64, p, p, p, p, p, p],
         "tq_ternarize": [p, i64, i64, p, p, p, p],
         "tq_attn_decode": [p, p, p, i64, i64, i64, i64, f32, p, p, ctypes.c_size_t, p],
+        "tq_attn_decode_noalloc": [p, p, p, i64, i64, i64, i64, f32, p, p],
         "tq_rmsnorm_act_quant": [p, i32, p, f32, i64, i64, p, p, p],
         "tq_pack3": [p, i64, i64, p, p],
         "tq_gemv3": [p, f32, p, p, i64, i64, p, p, p],
@@ -498,6 +499,34 @@ def tq_attn_decode(q, k_cache, v_cache, scale=None, out=None, workspace=None,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), H, Hkv, D, L, float(scale),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+TQ_ATTN_NOALLOC_MAX_H = 64
+
+
+def tq_attn_decode_noalloc(q, k_cache, v_cache, scale=None, out=None, stream=None):
+    """tq_attn_decode with the library's fixed per-GPU scratch instead of a
+    workspace (H <= 64): the call allocates nothing on the device when `out`
+    is passed.  Calls that may overlap in time on one GPU must not be
+    issued (they share that scratch)."""
+    torch = _torch()
+    _need(q, "q", torch.float32)
+    dev = q.device
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    if q.dim() != 2 or k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
+        raise ValueError("need q [H, D] and k/v [L, Hkv, D]")
+    H, D = q.shape
+    L, Hkv, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head dims differ")
+    if scale is None:
+        scale = ctypes.c_float(1.0 / math.sqrt(D)).value
+    out = _out(out, "out", (H, D), torch.float32, dev)
+    _check("tq_attn_decode_noalloc", lib.tq_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), H, Hkv, D, L, float(scale),
+        _ptr(out), _stream(stream)))
     return out
 
 

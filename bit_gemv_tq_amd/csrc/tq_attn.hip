@@ -31,6 +31,8 @@
 // three memory round trips on this chip, against one launch gap here.
 #include <math.h>
 
+#include <mutex>
+
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -505,6 +507,76 @@ extern "C" tq_status tq_attn_decode(const float *q, const void *k_cache,
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
   auto *part = static_cast<float *>(workspace);
+  return D == 128 ? launch_attn_d<128>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
+                                       (int)L, scale, out, part, stream)
+                  : launch_attn_d<64>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
+                                      (int)L, scale, out, part, stream);
+}
+
+// ---------------------------------------------------------------------------
+// tq_attn_decode_noalloc: the same kernels with the per-chunk partials in a
+// fixed device array instead of a caller workspace, for callers that cannot
+// allocate.  Room for TQ_ATTN_NOALLOC_MAX_H query heads x kAttnMaxSplits
+// chunks x (128 + 4) floats; each GPU holds its own copy for the life of the
+// process.  The chunk pass writes every partial the combine pass reads, so
+// nothing has to start at zero.
+namespace tq {
+namespace {
+constexpr size_t kScratchFloats =
+    (size_t)TQ_ATTN_NOALLOC_MAX_H * kAttnMaxSplits * (128 + 4);
+static_assert(kScratchFloats * 4 == TQ_ATTN_NOALLOC_SCRATCH_BYTES,
+              "scratch size in the header");
+}  // namespace
+}  // namespace tq
+
+static __device__ __align__(256) float scratch[tq::kScratchFloats];
+
+namespace tq {
+namespace {
+// Device address of this GPU's copy of `scratch`.  In host code the array's
+// name is only a stand-in: the address comes from the runtime, once per
+// device (with that device current), and is kept.
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices];
+
+tq_status scratch_address(int dev, float **out) {
+  if (dev < 0 || dev >= kScratchDevices) return TQ_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return TQ_ERR_DEVICE;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float *>(g_scratch_ptr[dev]);
+  return TQ_OK;
+}
+}  // namespace
+}  // namespace tq
+
+extern "C" tq_status tq_attn_decode_noalloc(const float *q, const void *k_cache,
+                                            const void *v_cache, int64_t H,
+                                            int64_t Hkv, int64_t D, int64_t L,
+                                            float scale, float *out,
+                                            hipStream_t stream) {
+  using namespace tq;
+  if (H < 1 || Hkv < 1 || H % Hkv != 0 || H > TQ_ATTN_NOALLOC_MAX_H) return TQ_ERR_SHAPE;
+  const int64_t G = H / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_ERR_SHAPE;
+  if (D != 64 && D != 128) return TQ_ERR_SHAPE;
+  if (L < 1 || L > TQ_ATTN_MAX_L) return TQ_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !out) return TQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 4))
+    return TQ_ERR_ALIGN;
+  DeviceInfo dev;
+  if (tq_status s = current_device(&dev)) return s;
+  float *part = nullptr;
+  if (tq_status s = scratch_address(dev.device, &part)) return s;
+  // At most kAttnMaxSplits chunks of H rows of D + 4 floats are written.
   return D == 128 ? launch_attn_d<128>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
                                        (int)L, scale, out, part, stream)
                   : launch_attn_d<64>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,

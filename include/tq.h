@@ -42,7 +42,8 @@
  * Memory and streams:
  *   - Every array argument is caller-owned DEVICE memory on the current HIP
  *     device.  The library allocates and frees nothing and keeps no state
- *     beyond a per-device cache of the compute-unit count.
+ *     beyond a per-device cache of the compute-unit count (and the fixed
+ *     device array of tq_attn_decode_noalloc, with its per-device address).
  *   - Every call enqueues its work on `stream` (NULL = the default stream)
  *     and returns without synchronizing.  Calls are thread-safe.
  *
@@ -341,6 +342,30 @@ TQ_API tq_status tq_attn_decode(const float *q, const void *k_cache,
                                 int64_t D, int64_t L, float scale, float *out,
                                 void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/*
+ * tq_attn_decode_noalloc -- tq_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, and the call
+ * allocates nothing.  The per-chunk partials live in a fixed device array
+ * of TQ_ATTN_NOALLOC_SCRATCH_BYTES inside the library (one copy per GPU,
+ * held until the process ends; its address is looked up once per device on
+ * the first call there).  Same kernels, so the output is bit-identical to
+ * tq_attn_decode's.
+ *   q, k_cache, v_cache, H, Hkv, D, L, scale, out: as tq_attn_decode.
+ *   H  1..TQ_ATTN_NOALLOC_MAX_H (larger H: TQ_ERR_SHAPE, nothing launched).
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (different streams, other threads) race and must not be
+ * issued; calls in order on one stream are safe.
+ */
+#define TQ_ATTN_NOALLOC_MAX_H 64
+#define TQ_ATTN_NOALLOC_SCRATCH_BYTES \
+  ((size_t)TQ_ATTN_NOALLOC_MAX_H * 64u * (128u + 4u) * 4u)
+TQ_API tq_status tq_attn_decode_noalloc(const float *q, const void *k_cache,
+                                        const void *v_cache, int64_t H,
+                                        int64_t Hkv, int64_t D, int64_t L,
+                                        float scale, float *out,
+                                        hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 /*

@@ -35,7 +35,8 @@ def test_header_declares_the_calls():
                           "tq_quant_gate_up_relu2", "tq_quant_gemv_group",
                           "tq_ternarize", "tq_attn_decode", "tq_rmsnorm_act_quant",
                           "tq_rmsnorm_quant_gemv", "tq_pack3", "tq_gemv3",
-                          "tq_stream_read", "tq_status_string"}
+                          "tq_stream_read", "tq_attn_decode_noalloc",
+                          "tq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(tq):
@@ -239,6 +240,30 @@ def test_attn_decode_validation(tq):
     assert f(A, MIS, A, 20, 5, 128, 16, 0.1, A, A, W, None) == ALIGN
     assert f(A, A, A, 20, 5, 128, 16, 0.1, ODD, A, W, None) == ALIGN
     assert f(A, A, A, 20, 5, 128, 16, 0.1, A, P(0x10008), W, None) == ALIGN
+
+
+def test_attn_decode_noalloc_validation(tq):
+    f = tq.lib.tq_attn_decode_noalloc
+    #        q  k  v   H  Hkv  D    L   scale  out stream
+    assert f(A, A, A, 72, 9, 128, 16, 0.1, A, None) == SHAPE      # H > 64
+    assert f(A, A, A, 128, 16, 64, 16, 0.1, A, None) == SHAPE     # H > 64
+    assert f(A, A, A, 20, 3, 128, 16, 0.1, A, None) == SHAPE      # H % Hkv
+    assert f(A, A, A, 48, 4, 128, 16, 0.1, A, None) == SHAPE      # group 12
+    assert f(A, A, A, 20, 5, 96, 16, 0.1, A, None) == SHAPE       # D
+    assert f(A, A, A, 20, 5, 128, 0, 0.1, A, None) == SHAPE       # L = 0
+    assert f(A, A, A, 20, 5, 128, 131073, 0.1, A, None) == SHAPE
+    assert f(None, A, A, 20, 5, 128, 16, 0.1, A, None) == NULL
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, None, None) == NULL
+    assert f(MIS, A, A, 20, 5, 128, 16, 0.1, A, None) == ALIGN
+    assert f(A, A, MIS, 20, 5, 128, 16, 0.1, A, None) == ALIGN
+    assert f(A, A, A, 20, 5, 128, 16, 0.1, ODD, None) == ALIGN
+
+
+def test_attn_noalloc_scratch_size():
+    # TQ_ATTN_NOALLOC_SCRATCH_BYTES: 64 heads x 64 chunks x (128 + 4) floats
+    text = open(HEADER).read()
+    assert "#define TQ_ATTN_NOALLOC_MAX_H 64" in text
+    assert 64 * 64 * 132 * 4 == 2162688
 
 
 def test_attn_workspace_size(tq):
