@@ -1,8 +1,9 @@
 // tq_gemv3.hip -- tq_pack3 and tq_gemv3: the M = 1 ternary GEMV on the denser
 // five-weights-per-byte layout (1.6 bits per weight).
 //
-// Page "1bit.systems" project README names the "TQ1_0" family of ternary
-// formats only; the layout is this library's reading.  The packed array is
+// Page "Feature request: BitNet 1.58-bit ternary inference on ROCm
+// (gfx1151)", section "Context", names the "TQ1_0" family of ternary formats
+// only; the layout is this library's reading.  The packed array is
 // [N5, K], N5 = ceil(N/5); byte [i,k] holds rows j*N5 + i (j = 0..4) of
 // column k as the base-3 number v = sum_j c_j 3^j of their codes c = w + 1
 // (rows past N are zero weights), stored as q = ceil(256 v / 243).

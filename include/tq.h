@@ -9,7 +9,8 @@
  *            as uint8, four values per byte; squared-ReLU MLP) and section
  *            "Weight mapping (bitnet-b1.58-2B-4T)" (a projection [N,K] is
  *            held as a [N/4,K] uint8 array; per-tensor .weight_scale keys
- *            are named in "What We Need").
+ *            are named in "What We Need"); section "Context" names the
+ *            TQ1_0 ternary format family.
  *   [ARC]    "the full arc: how the 1bit.systems ternary stack got from
  *            broken to 76.7 tok/s" -- TL;DR (a hand-tuned ternary GEMV
  *            near the memory-bandwidth peak is the decode hot loop).
@@ -56,7 +57,8 @@
  * Shape rules: N % 4 == 0; K % 16 == 0; 0 <= K <= TQ_MAX_K;
  * 1 <= M <= TQ_MAX_M where M is an argument.  N == 0 or M == 0 is a no-op
  * returning TQ_OK.  K == 0 is allowed (empty sums: acc = 0).
- * Alignment: packed, xq and x 16-byte aligned; y, acc, h, x_scale 4-byte.
+ * Alignment: packed, xq, x and the int8 weights of tq_pack / tq_pack3 16-byte
+ * aligned; y, acc, h, x_scale 4-byte.
  * Inputs must be finite; NaN/Inf activations are outside the contract.
  */
 #ifndef TQ_H
@@ -99,8 +101,9 @@ typedef enum tq_dtype {
 /*
  * tq_pack -- pack ternary weights ([ISSUE] "Architecture": uint8, four
  * values per byte; "Weight mapping": [N,K] -> [N/4,K]).
- *   w       int8 [N,K], values in {-1,0,1}; any other value is written as
- *           the reserved code 3 (outside the contract of every other call).
+ *   w       int8 [N,K], 16-byte aligned, values in {-1,0,1}; any other value
+ *           is written as the reserved code 3 (outside the contract of every
+ *           other call).
  *   packed  uint8 [N/4,K], output, 16-byte aligned.
  */
 TQ_API tq_status tq_pack(const int8_t *w, int64_t N, int64_t K, uint8_t *packed,
@@ -108,8 +111,8 @@ TQ_API tq_status tq_pack(const int8_t *w, int64_t N, int64_t K, uint8_t *packed,
 
 /*
  * tq_pack3 -- the denser layout: five weights per byte, 1.6 bits per weight
- * ([README] names the "TQ1_0" family of such formats only; the layout is
- * this library's reading).  packed [N5, K], N5 = ceil(N/5); byte [i,k]
+ * ([ISSUE] section "Context" names the "TQ1_0" family of such formats
+ * only; the layout is this library's reading).  packed [N5, K], N5 = ceil(N/5); byte [i,k]
  * holds rows j*N5 + i (j = 0..4) of column k as the base-3 number
  * v = sum_j (w+1) 3^j (rows past N count as zero weights), stored as
  * q = ceil(256 v / 243).  13 byte values encode no v and are reserved.
@@ -367,7 +370,6 @@ TQ_API tq_status tq_attn_decode_noalloc(const float *q, const void *k_cache,
                                         float scale, float *out,
                                         hipStream_t stream);
 
-/* Static, human-readable text for a status code. */
 /*
  * tq_stream_read -- measurement helper: the practical HBM read ceiling that
  * the GEMV's weight stream is compared with ([ARC] TL;DR and [README]
@@ -387,6 +389,7 @@ TQ_API tq_status tq_attn_decode_noalloc(const float *q, const void *k_cache,
 TQ_API tq_status tq_stream_read(const void *buf, int64_t bytes, void *sink,
                                 int64_t sink_words, hipStream_t stream);
 
+/* Static, human-readable text for a status code. */
 TQ_API const char *tq_status_string(tq_status status);
 
 #ifdef __cplusplus

@@ -72,8 +72,9 @@ int tqo_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *w)
 
 /*
  * Denser packing: five ternary weights per byte, 1.6 bits per weight (the
- * page "1bit.systems" README names the "TQ1_0" family only; no layout is
- * given).  Reading used here: the packed array is [N5, K] with
+ * page "Feature request: BitNet 1.58-bit ternary inference on ROCm
+ * (gfx1151)", section "Context", names the "TQ1_0" family only; no layout
+ * is given).  Reading used here: the packed array is [N5, K] with
  * N5 = ceil(N/5); byte [i,k] holds rows j*N5 + i (j = 0..4) of column k as
  * the base-3 number v = sum_j c_j 3^j of their codes c = w + 1 (rows past N
  * are zero weights, c = 1), stored as the byte q = ceil(256 v / 243).  v is

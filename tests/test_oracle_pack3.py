@@ -1,5 +1,6 @@
 """Pins of the oracle's five-weights-per-byte packing (the denser variant:
-the page "1bit.systems" README names the TQ1_0 family only, so the layout is
+the page "Feature request: BitNet 1.58-bit ternary inference on ROCm
+(gfx1151)", section "Context", names the TQ1_0 family only, so the layout is
 this build's reading; see the fixture for it).
 
 Checked against a hand-derived fixture, exhaustively over all 3^5 columns,

@@ -107,3 +107,29 @@ def test_argument_checks():
         oracle.rmsnorm_act_quant(x, np.ones(16, np.float32), 0.0, "f32")   # eps > 0
     with pytest.raises(ValueError):
         oracle.rmsnorm_act_quant(x, np.ones(8, np.float32), 1e-5, "f32")
+
+
+def test_folded_codes_equal_normalize_then_quantize():
+    """The folded reading (codes of x*gamma, the RMS factor r in the scale)
+    against the plain order -- normalize first, n = (x*r)*gamma in fp32, then
+    quantize n by its own absmax -- on 60 seeded bf16 rows with outliers at
+    the hidden sizes K = 2560, 6912, 28672: every code is the same, and the
+    two scales agree to a few fp32 ulps.  Absmax quantization is scale
+    invariant in exact arithmetic; this pins that the fp32 roundings of
+    either order do not move a code on these rows."""
+    total = 0
+    for K in (2560, 6912, 28672):
+        for r in range(20):
+            xb = workloads.activations_bf16(1, K, seed=7000 + K + r, outliers=True)
+            rng = np.random.default_rng(8000 + K + r)
+            gb = bf16((1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32))
+            q, s = oracle.rmsnorm_act_quant(xb, gb, 1e-5, "bf16")
+            x, g = from_bf16(xb)[0], from_bf16(gb)
+            ms = np.mean(x.astype(np.float64) ** 2) + np.float64(np.float32(1e-5))
+            r32 = np.float32(1.0 / np.sqrt(ms))
+            n = ((x * r32).astype(np.float32) * g).astype(np.float32)
+            qp, sp = oracle.act_quant(n[None, :], "f32")
+            np.testing.assert_array_equal(qp, q)
+            assert abs(float(sp[0]) - float(s[0])) <= 4 * np.spacing(np.float32(s[0]))
+            total += K
+    assert total == 762880
