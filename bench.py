@@ -13,28 +13,32 @@ by tq_pack; bf16 N(0,1) activations.  Everything is resident in HBM before
 timing starts.
 
 Timing:
-  * Each shape has a pool of distinct packed copies of at least 640 MB, so
-    the 256 MB Infinity Cache cannot serve repeats; step i uses copy i mod C.
+  * Each shape has a pool of distinct packed copies of at least 1 GiB, so
+    the 256 MB Infinity Cache cannot serve repeats: step i uses copy
+    i mod C of every pool (C = the pool's copy count).
   * Steps and kernel loops are captured in HIP graphs; a spin kernel queued
     before the start event keeps the host ahead, so HIP events on the
     launch stream measure GPU execution only.  A step graph holds 12
-    consecutive steps (one pass over the copies), so the fixed cost of a
-    graph replay (about 5 us) is spread as in a decode graph of a layer
+    consecutive steps (graph g: steps 12g .. 12g + 11), so the fixed cost of
+    a graph replay (about 5 us) is spread as in a decode graph of a layer
     stack; the time with one step per graph is reported too.
   * roofline: the dominant kernel (the fused [8192, 28672] launch) is timed
-    as a graph of back-to-back launches over its pool; algorithmic bytes per
-    launch (packed weights + bf16 x + int8 x written + fp32 scale + fp32 y)
-    / time per launch, against 8 TB/s.  Back-to-back time includes the short gap
-    between graph nodes, so it is an upper bound on the kernel duration
-    that rocprofv3's kernel trace reports.  Beside it, the measured read
-    ceiling: tq_stream_read (the same 16-byte non-temporal loads and nothing
-    else) over the same pool, and the kernel's fraction of it.
+    as graphs of 96 back-to-back launches over its pool; algorithmic bytes
+    per launch (packed weights + bf16 x + int8 x written + fp32 scale +
+    fp32 y) / time per launch, against 8 TB/s.  Beside it, the measured
+    read ceiling: tq_stream_read (16-byte non-temporal loads and nothing
+    else) over the same pool (one 58.7 MB buffer per launch) and over one
+    2 GiB buffer (the asymptotic rate, without the fixed cost of a launch).
+  * per_shape: the step's shapes plus the 8B-class layers [14336, 4096] and
+    [4096, 14336] and the 70B-class shards of an 8-way tensor-parallel split
+    ([3584, 8192] gate/up, [8192, 3584] down), fused and int8 GEMV each.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
     gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64), the absmean
     ternarizer, split-KV decode attention and the 30-layer decode-step chain
     (graph-captured).
-  * cpu_baseline: the CPU oracle (plain C, one thread) on one step, repeated
-    for about 10 s.
+  * cpu_baseline: the CPU oracle (plain C) on the same step, once on one
+    thread and once on every host core the process may use (output rows
+    split over threads), about 10 s each; `value` is the all-core rate.
 Prints one JSON line on stdout; progress on stderr.
 """
 from __future__ import annotations
@@ -56,13 +60,18 @@ METRIC = ("ternary GEMV weight GB/s + % of MI355X HBM peak at M=1 "
           "(2560x6912, 8192x28672)")
 SHAPES = {"down_2b4t": (2560, 6912), "70b_down": (8192, 28672),
           "70b_up": (28672, 8192)}
+# timed per shape beside the step: 8B-class layers, 70B-class TP=8 shards
+EXTRA_SHAPES = {"8b_up": (14336, 4096), "8b_down": (4096, 14336),
+                "70b_tp8_gate_up": (3584, 8192), "70b_tp8_down": (8192, 3584)}
 DOMINANT = "70b_down"
 HBM_PEAK_GBS = 8000.0
 INT8_MFMA_PEAK_TOPS = 5000.0
-POOL_BYTES_MIN = 640 << 20
-STEP_COPIES = 12
+POOL_BYTES_MIN = 1 << 30
+STEP_COPIES = 12        # steps per graph
+BIG_READ_BYTES = 2 << 30
 SPIN = 20_000_000
 COUNTER_FILE = os.path.join(ROOT, "profiles", "tq_quant_gemv_8192x28672_counters.txt")
+TRACE_FILE = os.path.join(ROOT, "profiles", "bench_kernel_trace.txt")
 KERNEL_SOURCES = ("bit_gemv_tq_amd/csrc/tq_gemv_reg.h",
                   "bit_gemv_tq_amd/csrc/tq_gemv.hip",
                   "bit_gemv_tq_amd/csrc/tq_device.h")
@@ -105,26 +114,79 @@ def kernel_source_hash(read=None):
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per dominant-kernel launch from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    if not os.path.exists(COUNTER_FILE):
+def read_profile(path):
+    """key: value fields of a committed rocprofv3 summary, or None unless it
+    was taken on the current kernel source."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(COUNTER_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
+    return fields
+
+
+def read_traffic():
+    """HBM bytes per dominant-kernel launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    f = read_profile(COUNTER_FILE)
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(f["hbm_bytes_per_launch"]) if f else None
     except (KeyError, ValueError):
         return None
 
 
-def cpu_baseline(budget_s=10.0):
-    """The CPU oracle on one step of the same workload."""
+def read_trace():
+    """The dominant kernel's rocprofv3 kernel-trace average and median (us),
+    if the committed trace was taken on the current kernel source."""
+    f = read_profile(TRACE_FILE)
+    try:
+        return (float(f["dominant_trace_avg_us"]),
+                float(f["dominant_trace_median_us"])) if f else None
+    except (KeyError, ValueError):
+        return None
+
+
+def trace_fields(tr, nbytes):
+    """The committed kernel-trace figures of the dominant kernel (when taken
+    on the current kernel source), with the fraction of peak they give."""
+    if tr is None:
+        return None
+    avg, med = tr
+    return {"avg_us": avg, "median_us": med,
+            "frac_from_avg": round(nbytes / avg / 1e3 / HBM_PEAK_GBS, 4),
+            "frac_from_median": round(nbytes / med / 1e3 / HBM_PEAK_GBS, 4),
+            "file": os.path.relpath(TRACE_FILE, ROOT)}
+
+
+def cpu_info():
+    model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return model, os.cpu_count(), usable
+
+
+def cpu_baseline(budget_s=10.0, max_threads=16):
+    """The CPU oracle on the same step: one thread, then all usable cores
+    (at most `max_threads`: the host share of one GPU) with each GEMV's
+    packed rows split into contiguous slices, one oracle call per slice on
+    its own thread (the oracle is plain C called through ctypes, which
+    releases the GIL, so the calls run in parallel).  The oracle itself is
+    unchanged; each output row is still summed by one thread."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
@@ -136,21 +198,43 @@ def cpu_baseline(budget_s=10.0):
         del codes
         xbits[name] = workloads.activations_bf16(1, K, seed=workloads.seed_for(5, 10 + t))
     s_w = np.float32(0.02)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for name, (N, K) in SHAPES.items():
-            q, s = oracle.act_quant(xbits[name], "bf16")
-            oracle.gemv(packed[name], s_w, q, s, N)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
-            break
+    model, ncpu, usable = cpu_info()
+    threads = max(1, min(usable, max_threads))
+    pool = ThreadPoolExecutor(threads)
+
+    def gemv_split(name, N, q, s, nt):
+        n4 = N // 4
+        cuts = [n4 * i // nt for i in range(nt + 1)]
+        jobs = [pool.submit(oracle.gemv, packed[name][a:b], s_w, q, s, 4 * (b - a))
+                for a, b in zip(cuts, cuts[1:]) if b > a]
+        return [j.result() for j in jobs]
+
+    def run(nt):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for name, (N, K) in SHAPES.items():
+                q, s = oracle.act_quant(xbits[name], "bf16")
+                if nt == 1:
+                    oracle.gemv(packed[name], s_w, q, s, N)
+                else:
+                    gemv_split(name, N, q, s, nt)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 400:
+                return reps, el
+
     step_bytes = sum(weight_bytes(*s) for s in SHAPES.values())
-    return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": (f"{reps} full steps (all three shapes, act_quant + GEMV) "
-                       f"in {el:.1f} s on one thread ({platform.machine()}, "
-                       f"{os.cpu_count()} host cores visible)")}
+    r1, e1 = run(1)
+    rn, en = run(threads)
+    pool.shutdown()
+    one = step_bytes * r1 / e1 / 1e9
+    alln = step_bytes * rn / en / 1e9
+    return {"value": round(alln, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{rn} full steps (all three shapes, act_quant + GEMV) in {en:.1f} s "
+                       f"on {threads} threads, output rows split over threads; "
+                       f"one thread: {r1} steps in {e1:.1f} s"),
+            "one_thread_value": round(one, 4),
+            "host": {"cpu_model": model, "nproc": ncpu, "usable_cores": usable}}
 
 
 def cpu_rows(budget_s=3.0):
@@ -248,20 +332,16 @@ class Timer:
         torch.cuda.synchronize()
         return g
 
-    def time_steps(self, multi, singles, steps):
-        """ms per step for exactly `steps` steps: `multi` holds len(singles)
-        consecutive steps, replayed steps // S times, then the remainder as
-        one-step graphs."""
+    def time_sequence(self, graphs, steps):
+        """ms per step: `graphs` (together exactly `steps` steps) replayed
+        once each, in order."""
         torch = self.torch
-        S = len(singles)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(SPIN)
         e0.record()
-        for _ in range(steps // S):
-            multi.replay()
-        for i in range(steps % S):
-            singles[i].replay()
+        for g in graphs:
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
@@ -333,66 +413,79 @@ def main():
             del w
         return out
 
+    ALL = dict(SHAPES, **EXTRA_SHAPES)
     pools = {}
-    for t, (name, (N, K)) in enumerate(SHAPES.items()):
+    for t, (name, (N, K)) in enumerate(ALL.items()):
         copies = max(STEP_COPIES, -(-POOL_BYTES_MIN // weight_bytes(N, K)))
         log(f"pool {name}: {copies} copies x {weight_bytes(N, K) / 1e6:.1f} MB")
         pools[name] = make_pool(N, K, copies, workloads.seed_for(4, t) * 1000 + 7)
     torch.cuda.synchronize()
     x, xq, xs, y = {}, {}, {}, {}
-    for t, (name, (N, K)) in enumerate(SHAPES.items()):
+    for t, (name, (N, K)) in enumerate(ALL.items()):
         xb = workloads.activations_bf16(1, K, seed=workloads.seed_for(4, 20 + t))
         x[name] = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)[0]
         xq[name] = torch.empty(K, dtype=torch.int8, device=dev)
         xs[name] = torch.empty(1, dtype=torch.float32, device=dev)
         y[name] = torch.empty(N, dtype=torch.float32, device=dev)
 
-    def step(i):
+    def step(i):  # step i reads copy i mod C of every pool
         for name in SHAPES:
-            tq.tq_quant_gemv(x[name], pools[name][i % STEP_COPIES], s_w, y[name],
+            P = pools[name]
+            tq.tq_quant_gemv(x[name], P[i % len(P)], s_w, y[name],
                              xq=xq[name], x_scale=xs[name])
 
     def step_unfused(i):
         for name in SHAPES:
+            P = pools[name]
             tq.tq_act_quant(x[name], xq[name], xs[name])
-            tq.tq_gemv(pools[name][i % STEP_COPIES], s_w, xq[name], xs[name], y[name])
+            tq.tq_gemv(P[i % len(P)], s_w, xq[name], xs[name], y[name])
 
-    def steps_of(fn):
-        # STEP_COPIES consecutive steps, one pass over the weight copies
+    def steps_of(fn, i0, n):
         def run():
-            for i in range(STEP_COPIES):
+            for i in range(i0, i0 + n):
                 fn(i)
         return run
 
+    def step_graphs(fn, steps):
+        """Graphs for steps 0 .. steps-1: STEP_COPIES consecutive steps per
+        graph (3 kernel nodes each, as a decode graph holds a whole layer
+        stack: a graph replay has a fixed cost of about 5 us on this part,
+        which a graph of one 3-kernel step would charge to every step), the
+        remainder as one-step graphs."""
+        S = STEP_COPIES
+        full = [timer.graph(steps_of(fn, g * S, S)) for g in range(steps // S)]
+        rest = [timer.graph(steps_of(fn, (steps // S) * S + j, 1)) for j in range(steps % S)]
+        return full + rest
+
+    def warm(graphs, warmup):
+        done = 0
+        for g in graphs:
+            if done >= warmup:
+                break
+            g.replay()
+            done += STEP_COPIES
+        torch.cuda.synchronize()
+
     # ---------------------------------------------------------------- step
-    # One graph holds STEP_COPIES consecutive steps (3 * STEP_COPIES kernel
-    # nodes, as a decode graph holds a whole layer stack): each graph replay
-    # has a fixed launch cost of about 5 us on this part, which a graph of
-    # one 3-kernel step would charge to every step.  The one-step-per-graph
-    # time is reported beside it.
     log("capturing step graphs")
-    singles = [timer.graph(lambda i=i: step(i)) for i in range(STEP_COPIES)]
-    multi = timer.graph(steps_of(step))
-    for _ in range(args.warmup // STEP_COPIES):
-        multi.replay()
-    for i in range(args.warmup % STEP_COPIES):
-        singles[i].replay()
-    torch.cuda.synchronize()
+    graphs = step_graphs(step, args.steps)
+    warm(graphs, args.warmup)
     wall0 = time.perf_counter()
-    ms_step = timer.time_steps(multi, singles, args.steps)
+    ms_step = timer.time_sequence(graphs, args.steps)
     wall = time.perf_counter() - wall0
     step_wbytes = sum(weight_bytes(*s) for s in SHAPES.values())
     value = step_wbytes / (ms_step * 1e-3) / 1e9
     log(f"step: {ms_step * 1e3:.2f} us -> {value:.0f} GB/s")
+    del graphs
+    singles = [timer.graph(steps_of(step, i, 1)) for i in range(STEP_COPIES)]
     ms_step_1 = timer.time_graphs(singles, args.steps)
     log(f"step, one step per graph: {ms_step_1 * 1e3:.2f} us")
-    del singles, multi
-    singles_u = [timer.graph(lambda i=i: step_unfused(i)) for i in range(STEP_COPIES)]
-    multi_u = timer.graph(steps_of(step_unfused))
-    multi_u.replay()
-    ms_step_u = timer.time_steps(multi_u, singles_u, args.steps)
+    del singles
+    graphs_u = step_graphs(step_unfused, args.steps)
+    warm(graphs_u, STEP_COPIES)
+    ms_step_u = timer.time_sequence(graphs_u, args.steps)
     log(f"unfused step (act_quant + gemv launches): {ms_step_u * 1e3:.2f} us")
-    del singles_u, multi_u
+    del graphs_u
 
     # ------------------------------------------------- per-kernel loops
     R = args.kernel_reps
@@ -416,11 +509,12 @@ def main():
                 tq.tq_gemv(P[(start + r) % len(P)], s_w, xq[name], xs[name], y[name])
 
     per_shape = {}
-    for name, (N, K) in SHAPES.items():
+    for name, (N, K) in ALL.items():
         tq.tq_act_quant(x[name], xq[name], xs[name])
         nP = len(pools[name])
-        row = {"N": N, "K": K}
-        for mode in ("quant_gemv", "gemv", "rmsnorm_quant_gemv"):
+        row = {"N": N, "K": K, "pool_copies": nP}
+        modes = ("quant_gemv", "gemv") + (("rmsnorm_quant_gemv",) if name in SHAPES else ())
+        for mode in modes:
             fused = mode != "gemv"
             gs = [timer.graph(lambda name=name, s=s, m=mode: gemv_loop(name, s, m))
                   for s in range(0, nP, max(1, nP // 4))][:4]
@@ -458,6 +552,22 @@ def main():
                "pct_hbm_peak": round(100 * read_gbs / HBM_PEAK_GBS, 1),
                "bytes": weight_bytes(dN, dK)}
     log(f"read ceiling over the {DOMINANT} pool: {ceiling}")
+    # ... and over one 2 GiB buffer per launch: the asymptotic read rate,
+    # where the fixed cost of a launch (dispatch, first-load latency, drain)
+    # no longer counts
+    big = torch.ones(BIG_READ_BYTES, dtype=torch.uint8, device=dev)
+
+    def big_loop():
+        for _ in range(8):
+            tq.tq_stream_read(big, sink)
+    g = timer.graph(big_loop)
+    big_us = timer.time_graphs([g], 2) * 1e3 / 8
+    del g, big
+    ceiling["large_buffer"] = {"us_per_launch": round(big_us, 2), "bytes": BIG_READ_BYTES,
+                               "GBs": round(BIG_READ_BYTES / big_us / 1e3, 1),
+                               "pct_hbm_peak": round(100 * BIG_READ_BYTES / big_us / 1e3
+                                                     / HBM_PEAK_GBS, 1)}
+    log(f"read ceiling over one 2 GiB buffer: {ceiling['large_buffer']}")
 
     rows = {}
     if not args.no_rows:
@@ -487,7 +597,8 @@ def main():
                          "[8192,28672] and [28672,8192] (70B-class, both "
                          "orientations); per shape act_quant(bf16) + gemv per step"),
             "weight_bytes_per_step": step_wbytes,
-            "pool_copies_per_shape": {k: len(v) for k, v in pools.items()},
+            "pool_copies_per_shape": {k: len(pools[k]) for k in SHAPES},
+            "pool_bytes_min": POOL_BYTES_MIN,
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
             "steps_per_graph": STEP_COPIES,
@@ -504,6 +615,9 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": read_traffic(),
             "us_per_launch": dom_us,
+            "time_source": ("live: HIP events around graphs of 96 back-to-back "
+                            "launches cycling the 1 GiB pool, divided by the launch count"),
+            "trace": trace_fields(read_trace(), algo_bytes_fused(dN, dK)),
             "bytes_per_launch": algo_bytes_fused(dN, dK),
             "read_ceiling_GBs": round(read_gbs, 1),
             "frac_of_read_ceiling": round(achieved / read_gbs, 4),

@@ -291,9 +291,8 @@ constexpr int quad_lds(int rg, int nq, int nm, int w) {
 
 // Quads per block: the largest RG that still gives about 5/8 of a block per
 // CU (measured on MI355X: a larger RG re-reads less of the activation tile,
-// too few blocks leave CUs idle).  Groups per wave and pass: the fewest
-// passes over K with at most 16 waves, within the register table above and
-// the LDS, ties to the smaller NQ.
+// too few blocks leave CUs idle).  Then one group per wave and pass, with
+// as many waves as the register table above and the LDS allow.
 QuadPlan plan_quad(int64_t M, int64_t n4, int64_t K, bool gate, int num_cus, int &mtiles) {
   const int nm = gate ? 2 : 1;
   mtiles = (int)((M + 15) / 16);
@@ -309,19 +308,17 @@ QuadPlan plan_quad(int64_t M, int64_t n4, int64_t K, bool gate, int num_cus, int
     return nq <= quad_max_nq(nm, pl.rg, w > 8 ? 16 : 8) &&
            quad_lds(pl.rg, nq, nm, w) <= kLdsBytes;
   };
+  // One 256-byte group per wave and pass, as many waves as the registers
+  // and LDS allow (up to one per group): more waves hide more latency than
+  // more groups per wave do.  Measured on MI355X, M = 64: [6912,2560]
+  // 6.4-6.5 us with 8 waves of one group (two passes) against 7.7-8.1 us
+  // with 5 waves of two (one pass); [2560,6912] 7.6-7.9 against 7.9-8.2 us
+  // with 16 waves of one group against 7 of four.
   const int64_t groups = (K + kGroup - 1) / kGroup;
-  int64_t best = INT64_MAX;
-  for (int nq = 1; nq <= 4; ++nq) {
-    int w = (int)std::min<int64_t>(16, std::max<int64_t>(1, (groups + nq - 1) / nq));
-    while (w > 1 && !fits(nq, w)) --w;
-    if (!fits(nq, w)) continue;
-    const int64_t passes = (groups + (int64_t)w * nq - 1) / ((int64_t)w * nq);
-    if (passes < best) {
-      best = passes;
-      pl.nq = nq;
-      pl.w = w;
-    }
-  }
+  int w = (int)std::min<int64_t>(16, std::max<int64_t>(1, groups));
+  while (w > 1 && !fits(1, w)) --w;
+  pl.nq = 1;
+  pl.w = w;
   return pl;
 }
 
@@ -345,13 +342,8 @@ tq_status launch_quad_w(const QuadPlan &pl, const GemmArgs &a, dim3 grid, hipStr
 
 template <int RG, bool kGate>
 tq_status launch_quad_nq(const QuadPlan &pl, const GemmArgs &a, dim3 grid, hipStream_t s) {
-  switch (pl.nq) {
-    case 1: return launch_quad_w<RG, 1, kGate>(pl, a, grid, s);
-    case 2: return launch_quad_w<RG, 2, kGate>(pl, a, grid, s);
-    case 3: return launch_quad_w<RG, 3, kGate>(pl, a, grid, s);
-    case 4: return launch_quad_w<RG, 4, kGate>(pl, a, grid, s);
-  }
-  return TQ_ERR_LAUNCH;
+  // The planner takes one group per wave and pass (NQ = 1).
+  return pl.nq == 1 ? launch_quad_w<RG, 1, kGate>(pl, a, grid, s) : TQ_ERR_LAUNCH;
 }
 
 template <bool kGate>

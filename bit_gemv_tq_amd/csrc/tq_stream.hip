@@ -18,24 +18,31 @@ namespace {
 
 constexpr int kStreamThreads = 256;
 constexpr int kStreamUnroll = 8;    // 16-byte loads in flight per lane
-constexpr int kStreamPerCu = 4;     // resident blocks per CU
+constexpr int kStreamPerCu = 8;     // resident blocks per CU
 
+// Tiles of kStreamThreads * kStreamUnroll pieces, interleaved over the grid
+// and read without predicates; the pieces past the last whole tile are read
+// by the last block.  (Measured on MI355X over a 2 GiB buffer: 8 blocks per
+// CU 7.02 TB/s, 4 blocks 6.98, 16 loads per lane 6.64, 1024-thread blocks
+// 6.80, ordinary cached loads 6.27.)
 __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(
     const u32x4 *__restrict__ p, int64_t n16, u32x4 *__restrict__ sink) {
   __shared__ u32x4 wx[kStreamThreads / kWave];
   u32x4 x = {0u, 0u, 0u, 0u};
-  const int64_t stride = (int64_t)gridDim.x * kStreamThreads * kStreamUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kStreamThreads * kStreamUnroll + threadIdx.x;
-       base < n16; base += stride) {
+  constexpr int64_t kTile = (int64_t)kStreamThreads * kStreamUnroll;
+  const int64_t tiles = n16 / kTile;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const u32x4 *q = p + t * kTile + threadIdx.x;
     u32x4 v[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) {
-      const int64_t i = base + (int64_t)u * kStreamThreads;
-      v[u] = i < n16 ? __builtin_nontemporal_load(p + i) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < kStreamUnroll; ++u)
+      v[u] = __builtin_nontemporal_load(q + u * kStreamThreads);
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) x ^= v[u];
   }
+  if (blockIdx.x == gridDim.x - 1)
+    for (int64_t i = tiles * kTile + threadIdx.x; i < n16; i += kStreamThreads)
+      x ^= __builtin_nontemporal_load(p + i);
 #pragma unroll
   for (int off = kWave / 2; off >= 1; off >>= 1)
 #pragma unroll
@@ -65,7 +72,8 @@ extern "C" tq_status tq_stream_read(const void *buf, int64_t bytes, void *sink,
   if (tq_status s = current_device(&dev)) return s;
   const int64_t n16 = bytes / 16;
   const int64_t per_block = (int64_t)kStreamThreads * kStreamUnroll;
-  int64_t blocks = (n16 + per_block - 1) / per_block;
+  int64_t blocks = n16 / per_block;  // whole tiles; the last block also reads the rest
+  if (blocks < 1) blocks = 1;
   blocks = blocks < (int64_t)dev.num_cus * kStreamPerCu ? blocks : (int64_t)dev.num_cus * kStreamPerCu;
   blocks = blocks < sink_words ? blocks : sink_words;
   return launch(stream_read_kernel, dim3((unsigned)blocks), dim3(kStreamThreads), 0,

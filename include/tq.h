@@ -381,7 +381,7 @@ TQ_API tq_status tq_attn_decode_noalloc(const float *q, const void *k_cache,
  *   sink        device, 16-B aligned, `sink_words` 16-byte words.  Block b
  *               writes word b: the XOR of the 16-byte words it read, so the
  *               XOR of the written words equals the XOR of every 16-byte
- *               word of buf; at most min(sink_words, 4 x CUs) words are
+ *               word of buf; at most min(sink_words, 8 x CUs) words are
  *               written, the rest are left as they were.
  * Errors: TQ_ERR_SHAPE (bytes < 0, bytes % 16, sink_words < 1), TQ_ERR_NULL,
  * TQ_ERR_ALIGN, TQ_ERR_DEVICE, TQ_ERR_LAUNCH.

@@ -235,10 +235,10 @@ def test_gate_up_relu2(env, M, N, K):
 
 # ------------------------------------------------------------------ gemm small
 # M = 2 runs on the vector ALU (K <= 16384), M >= 3 on the matrix cores.
-# The matrix-core plans these shapes take (quads per block RG, groups per wave
-# NQ, waves W, passes over K): every RG in {1, 2, 4, 8}, NQ 1..4, W 1..16,
-# blocks of up to 8 and up to 16 waves, one to four passes, ragged K (not a
-# multiple of 256) and ragged N (not a multiple of 16 RG).
+# The matrix-core plans these shapes take (quads per block RG, one 256-byte
+# group per wave and pass, waves W, passes over K): every RG in {1, 2, 4, 8},
+# W 1..16, blocks of up to 8 and up to 16 waves, one to 32 passes, ragged K
+# (not a multiple of 256) and ragged N (not a multiple of 16 RG).
 GEMM_CASES = [(m, 6912, 2560) for m in (2, 3, 4, 8, 16, 32, 64)] + \
              [(m, 2560, 6912) for m in (2, 3, 4, 16, 32, 64)] + \
              [(3, 20, 48), (5, 68, 80), (17, 260, 400), (33, 100, 1008),
@@ -288,7 +288,7 @@ def test_gemm_small_zero_k(env):
 # pieces past the row end).
 FUSED_SHAPES = [(4, 16), (12, 48), (100, 1008), (36, 2064), (2560, 2560),
                 (6912, 2560), (2560, 6912), (8, 32768), (4, 32784), (28, 16384),
-                (28672, 8192), (8192, 28672), (8400, 20000)]
+                (28672, 8192), (8192, 28672), (8400, 20000), (14336, 4096)]
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)
