@@ -43,7 +43,7 @@
 
 namespace tq {
 
-tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
+tq_status gemv_m1(bool gate, const uint8_t *p0, float s0, const uint8_t *p1, float s1,
                   const int8_t *xq, const float *x_scale, int64_t N, int64_t K,
                   float *y, int32_t *acc0, int32_t *acc1, hipStream_t stream);
 // M = 2 on the vector ALU (tq_gemm_dot4.hip).
@@ -366,15 +366,15 @@ tq_status launch_gemm(GemmArgs a, int num_cus, hipStream_t s) {
   return TQ_ERR_LAUNCH;
 }
 
-tq_status gemm_small(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
+tq_status gemm_small(bool gate, const uint8_t *p0, float s0, const uint8_t *p1, float s1,
                      const int8_t *xq, const float *x_scale, int64_t M,
                      int64_t N, int64_t K, float *y, int32_t *acc0,
                      int32_t *acc1, hipStream_t stream) {
   if (M == 1)
-    return gemv_m1(p0, s0, p1, s1, xq, x_scale, N, K, y, acc0, acc1, stream);
+    return gemv_m1(gate, p0, s0, p1, s1, xq, x_scale, N, K, y, acc0, acc1, stream);
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
-  if (!p1 && gemm_dot4_fits(M, K))
+  if (!gate && gemm_dot4_fits(M, K))
     return gemm_dot4(p0, s0, xq, x_scale, M, N, K, y, acc0, dev.num_cus, stream);
   GemmArgs a;
   a.p0 = p0;
@@ -390,7 +390,7 @@ tq_status gemm_small(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
   a.acc0 = acc0;
   a.acc1 = acc1;
   a.ntiles = a.mtiles = a.per_xcd = 0;  // set by the launcher
-  return p1 ? launch_gemm<true>(a, dev.num_cus, stream)
+  return gate ? launch_gemm<true>(a, dev.num_cus, stream)
             : launch_gemm<false>(a, dev.num_cus, stream);
 }
 
@@ -418,7 +418,7 @@ extern "C" tq_status tq_gemm_small(const uint8_t *packed, float w_scale,
   if (tq_status s = check_common(packed, xq, x_scale, M, N, K, y, acc, nullptr))
     return s;
   if (M == 0 || N == 0) return TQ_OK;
-  return gemm_small(packed, w_scale, nullptr, 0.0f, xq, x_scale, M, N, K, y,
+  return gemm_small(false, packed, w_scale, nullptr, 0.0f, xq, x_scale, M, N, K, y,
                     acc, nullptr, stream);
 }
 
@@ -435,10 +435,6 @@ extern "C" tq_status tq_gate_up_relu2(const uint8_t *packed_gate, float s_gate,
   if (M == 0 || N == 0) return TQ_OK;
   if (K > 0 && !packed_up) return TQ_ERR_NULL;
   if (!aligned(packed_up, 16)) return TQ_ERR_ALIGN;
-  // The kernels tell the gated form by a non-null second stream; with K == 0
-  // both streams are empty, so any non-null stand-in keeps the gated path.
-  const uint8_t *pu = packed_up ? packed_up : packed_gate;
-  if (!pu) pu = reinterpret_cast<const uint8_t *>(h);
-  return gemm_small(packed_gate, s_gate, pu, s_up, xq, x_scale, M, N, K, h,
+  return gemm_small(true, packed_gate, s_gate, packed_up, s_up, xq, x_scale, M, N, K, h,
                     acc_gate, acc_up, stream);
 }

@@ -258,13 +258,13 @@ tq_status launch_gemv_reg(const RegPlan &pl, bool gate, int xt,
   return TQ_ERR_LAUNCH;
 }
 
-// Shared by tq_gemv and the M = 1 branch of tq_gate_up_relu2.
-tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
+// Shared by tq_gemv and the M = 1 branch of tq_gate_up_relu2 (gate: the
+// two-matrix form, p1 the up projection).
+tq_status gemv_m1(bool gate, const uint8_t *p0, float s0, const uint8_t *p1, float s1,
                   const int8_t *xq, const float *x_scale, int64_t N, int64_t K,
                   float *y, int32_t *acc0, int32_t *acc1, hipStream_t stream) {
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
-  const bool gate = p1 != nullptr;
   const int64_t n4 = N / 4, kp = K / 16;
   if (kp >= 1 && kp <= kRegMaxPieces) {
     RegArgs a{p0,  p1,   s0,   s1,      xq,      x_scale, (int)n4, (int)kp,
@@ -293,14 +293,13 @@ tq_status gemv_m1(const uint8_t *p0, float s0, const uint8_t *p1, float s1,
 
 // Per-token quantization of a raw activation row fused into the GEMV
 // prologue (one launch); K == 0 or K > 32768 take two launches.
-tq_status quant_gemv_m1(const void *x, tq_dtype xt, const uint8_t *p0,
+tq_status quant_gemv_m1(bool gate, const void *x, tq_dtype xt, const uint8_t *p0,
                         float s0, const uint8_t *p1, float s1, int64_t N,
                         int64_t K, float *y, int32_t *acc0, int32_t *acc1,
                         int8_t *xq, float *x_scale, const float *y_scale,
                         hipStream_t stream) {
   DeviceInfo dev;
   if (tq_status s = current_device(&dev)) return s;
-  const bool gate = p1 != nullptr;
   const int64_t n4 = N / 4, kp = K / 16;
   if (N > 0 && kp >= 1 && kp <= kRegMaxPieces) {
     RegArgs a{p0, p1,   s0,   s1, nullptr, nullptr, (int)n4, (int)kp,
@@ -311,7 +310,7 @@ tq_status quant_gemv_m1(const void *x, tq_dtype xt, const uint8_t *p0,
   }
   if (tq_status s = tq_act_quant(x, xt, 1, K, xq, x_scale, stream)) return s;
   if (N == 0) return TQ_OK;
-  return gemv_m1(p0, s0, p1, s1, xq, y_scale ? y_scale : x_scale, N, K, y,
+  return gemv_m1(gate, p0, s0, p1, s1, xq, y_scale ? y_scale : x_scale, N, K, y,
                  acc0, acc1, stream);
 }
 
@@ -335,7 +334,8 @@ tq_status rmsnorm_quant_gemv_m1(const void *x, tq_dtype xt, const void *gamma,
   if (tq_status s = rmsnorm_act_quant(x, xt, gamma, eps, 1, K, xq, x_scale, stream))
     return s;
   if (N == 0) return TQ_OK;
-  return gemv_m1(p0, s0, nullptr, 0.0f, xq, x_scale, N, K, y, acc0, nullptr, stream);
+  return gemv_m1(false, p0, s0, nullptr, 0.0f, xq, x_scale, N, K, y, acc0, nullptr,
+                 stream);
 }
 
 tq_status check_quant_args(const void *x, tq_dtype xt, const uint8_t *p,
@@ -394,7 +394,7 @@ tq_status quant_gemv_group(const void *x, tq_dtype xt, int count,
   if (tq_status s = tq_act_quant(x, xt, 1, K, xq, x_scale, stream)) return s;
   for (int i = 0; i < count; ++i) {
     if (N[i] == 0) continue;
-    if (tq_status s = gemv_m1(packed[i], w_scale[i], nullptr, 0.0f, xq,
+    if (tq_status s = gemv_m1(false, packed[i], w_scale[i], nullptr, 0.0f, xq,
                               y_scale ? y_scale : x_scale, N[i], K, y[i],
                               acc ? acc[i] : nullptr, nullptr, stream))
       return s;
@@ -438,7 +438,7 @@ extern "C" tq_status tq_quant_gemv(const void *x, tq_dtype xt,
   if (tq_status s = check_quant_args(x, xt, packed, N, K, y, acc, nullptr, xq,
                                      x_scale, y_scale))
     return s;
-  return quant_gemv_m1(x, xt, packed, w_scale, nullptr, 0.0f, N, K, y, acc,
+  return quant_gemv_m1(false, x, xt, packed, w_scale, nullptr, 0.0f, N, K, y, acc,
                        nullptr, xq, x_scale, y_scale, stream);
 }
 
@@ -468,10 +468,7 @@ extern "C" tq_status tq_quant_gate_up_relu2(
     return s;
   if (N > 0 && K > 0 && !packed_up) return TQ_ERR_NULL;
   if (!aligned(packed_up, 16)) return TQ_ERR_ALIGN;
-  // The kernels tell the gated form by a non-null second stream; with K == 0
-  // both streams are empty, so any non-null stand-in keeps the gated path.
-  const uint8_t *pu = packed_up ? packed_up : reinterpret_cast<const uint8_t *>(x_scale);
-  return quant_gemv_m1(x, xt, packed_gate, s_gate, pu, s_up, N, K, h, acc_gate,
+  return quant_gemv_m1(true, x, xt, packed_gate, s_gate, packed_up, s_up, N, K, h, acc_gate,
                        acc_up, xq, x_scale, y_scale, stream);
 }
 
@@ -486,6 +483,6 @@ extern "C" tq_status tq_gemv(const uint8_t *packed, float w_scale,
   if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(y, 4) ||
       !aligned(acc, 4) || !aligned(x_scale, 4))
     return TQ_ERR_ALIGN;
-  return gemv_m1(packed, w_scale, nullptr, 0.0f, xq, x_scale, N, K, y, acc,
+  return gemv_m1(false, packed, w_scale, nullptr, 0.0f, xq, x_scale, N, K, y, acc,
                  nullptr, stream);
 }

@@ -426,3 +426,29 @@ def test_quant_gemv_edges(env):
     torch.cuda.synchronize()
     assert not y.any()
     assert xs.cpu().numpy()[0] == np.float32(np.float32(1e-5) / np.float32(127))
+
+
+def test_gate_up_zero_k_without_up_matrix(env):
+    """K == 0 with no up matrix at all (a null pointer is allowed when there
+    is nothing to read): h = +0, for M = 1 and M > 1 and the fused form."""
+    torch, tq, _ = env
+    import ctypes
+    say("gate_up K=0, packed_up NULL")
+    lib = tq.lib
+    for M in (1, 5):
+        h = torch.full((M, 8), 7.0, device="cuda")
+        xs = torch.ones(M, dtype=torch.float32, device="cuda")
+        st = lib.tq_gate_up_relu2(None, 0.5, None, 0.25, None, ctypes.c_void_p(xs.data_ptr()),
+                                  M, 8, 0, ctypes.c_void_p(h.data_ptr()), None, None, None)
+        torch.cuda.synchronize()
+        assert st == 0
+        assert not h.cpu().numpy().view(np.uint32).any()
+    h = torch.full((8,), 7.0, device="cuda")
+    xs = torch.empty(1, dtype=torch.float32, device="cuda")
+    st = lib.tq_quant_gate_up_relu2(None, 0, None, 0.5, None, 0.25, 8, 0,
+                                    ctypes.c_void_p(h.data_ptr()), None, None, None,
+                                    ctypes.c_void_p(xs.data_ptr()), None, None)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert not h.cpu().numpy().view(np.uint32).any()
+    assert xs.item() == np.float32(np.float32(1e-5) / np.float32(127))
