@@ -31,7 +31,9 @@ Timing:
     2 GiB buffer (the asymptotic rate, without the fixed cost of a launch).
   * per_shape: the step's shapes plus the 8B-class layers [14336, 4096] and
     [4096, 14336] and the 70B-class shards of an 8-way tensor-parallel split
-    ([3584, 8192] gate/up, [8192, 3584] down), fused and int8 GEMV each.
+    ([3584, 8192] gate/up, [8192, 3584] down), fused and int8 GEMV each, with
+    the read ceiling at the same bytes per launch (tq_stream_read over the
+    same pool) and each form's fraction of it.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
     gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64), the absmean
     ternarizer, split-KV decode attention and the 30-layer decode-step chain
@@ -375,8 +377,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=96,
                     help="launches per graph in the per-kernel loops")
     ap.add_argument("--counters", action="store_true",
-                    help="only run a 256 MiB calibration copy and the dominant "
-                         "kernel (for rocprofv3 --pmc runs), then exit")
+                    help="only run a 256 MiB calibration copy, the dominant kernel, "
+                         "the int8 GEMV and the five-per-byte GEMV at its shape, 8 "
+                         "launches each (for rocprofv3 --pmc runs), then exit")
     ap.add_argument("--counters-gemm", action="store_true",
                     help="only run the small-batch GEMM at each benchmarked "
                          "(M, N, K), 8 launches each (for rocprofv3 --pmc runs)")
@@ -508,6 +511,13 @@ def main():
             else:
                 tq.tq_gemv(P[(start + r) % len(P)], s_w, xq[name], xs[name], y[name])
 
+    sink = torch.zeros(4096, 4, dtype=torch.int32, device=dev)
+
+    def read_pool_loop(name, start):
+        P = pools[name]
+        for r in range(R):
+            tq.tq_stream_read(P[(start + r) % len(P)], sink)
+
     per_shape = {}
     for name, (N, K) in ALL.items():
         tq.tq_act_quant(x[name], xq[name], xs[name])
@@ -528,6 +538,15 @@ def main():
                 "pct_hbm_peak": round(100 * weight_bytes(N, K) / us / 1e3 / HBM_PEAK_GBS, 1),
                 "algo_GBs": round(ab / us / 1e3, 1)}
             del gs
+        # the read ceiling at this shape: tq_stream_read over the same pool,
+        # one packed matrix per launch (the same bytes and launch count)
+        gs = [timer.graph(lambda name=name, s=s: read_pool_loop(name, s))
+              for s in range(0, nP, max(1, nP // 4))][:4]
+        rus = timer.time_graphs(gs, 8) * 1e3 / R
+        del gs
+        row["read_ceiling_us"] = round(rus, 3)
+        for mode in modes:
+            row[mode]["frac_of_read_ceiling"] = round(rus / row[mode]["us_per_launch"], 3)
         per_shape[name] = row
         log(f"{name}: {row}")
 
@@ -537,16 +556,7 @@ def main():
 
     # the measured read ceiling: a read-only kernel (tq_stream_read, the
     # GEMV's 16-byte non-temporal access and nothing else) over the same pool
-    sink = torch.zeros(4096, 4, dtype=torch.int32, device=dev)
-
-    def read_loop(start):
-        P = pools[DOMINANT]
-        for r in range(R):
-            tq.tq_stream_read(P[(start + r) % len(P)], sink)
-    nP = len(pools[DOMINANT])
-    gs = [timer.graph(lambda s=s: read_loop(s)) for s in range(0, nP, max(1, nP // 4))][:4]
-    read_us = timer.time_graphs(gs, 8) * 1e3 / R
-    del gs
+    read_us = per_shape[DOMINANT]["read_ceiling_us"]
     read_gbs = weight_bytes(dN, dK) / read_us / 1e3
     ceiling = {"us_per_launch": round(read_us, 3), "GBs": round(read_gbs, 1),
                "pct_hbm_peak": round(100 * read_gbs / HBM_PEAK_GBS, 1),
@@ -630,9 +640,11 @@ def main():
 
 
 def counters_run(torch, tq, workloads, dev):
-    """Dispatches for the HBM-traffic counters: a plain device-to-device copy
-    of 256 MiB (calibration: its FETCH_SIZE and WRITE_SIZE should each read
-    256 MiB), then the dominant GEMV over 4 distinct weight copies."""
+    """Dispatches for the HBM-traffic and instruction counters: a plain
+    device-to-device copy of 256 MiB (calibration: its FETCH_SIZE and
+    WRITE_SIZE should each read 256 MiB), then the dominant GEMV over 4
+    distinct weight copies, the int8 GEMV on them, and the five-per-byte
+    GEMV at the same shape."""
     import numpy as np
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
@@ -654,6 +666,21 @@ def counters_run(torch, tq, workloads, dev):
     torch.cuda.synchronize()
     for r in range(8):
         tq.tq_quant_gemv(xt, P[r % 4], 0.02, yy, xq=q, x_scale=s)
+    torch.cuda.synchronize()
+    # the int8 GEMV on the same weights, then the five-per-byte GEMV on the
+    # same shape (four distinct copies each)
+    for r in range(8):
+        tq.tq_gemv(P[r % 4], 0.02, q, s, yy)
+    torch.cuda.synchronize()
+    del P
+    P3 = []
+    for c in range(4):
+        w = workloads.ternary_codes_torch(N, K, seed=4342 + c, device=dev)
+        P3.append(tq.tq_pack3(w))
+        del w
+    torch.cuda.synchronize()
+    for r in range(8):
+        tq.tq_gemv3(P3[r % 4], 0.02, q, s, N, yy)
     torch.cuda.synchronize()
     log("counters run done")
 

@@ -356,3 +356,65 @@ def test_gemv3_closed_forms(env, K, N):
             check_closed(wkind, got, q_ref)
             np.testing.assert_array_equal(y.cpu().numpy()[None, :].view(np.uint32),
                                           y32[:, :n].view(np.uint32))
+
+
+# ------------------------------------------------------------------ grouped, RMSNorm
+@pytest.mark.parametrize("K", [2560, 32768, 32784])
+def test_quant_gemv_group_closed_forms(env, K):
+    """Several matrices sharing one activation row (the q/k/v launch), each a
+    different structured pattern, in one launch (K > 32768: its fallback)."""
+    torch, tq, oracle = env
+    kinds = ("plus", "minus", "zero")
+    Ns = (36, 20, 12)
+    scales = [np.float32(0.02), np.float32(0.021), np.float32(0.022)]
+    for akind in ("all127", "alt127"):
+        bits = act_rows(akind, 1, K)
+        x = dev_bf16(env, bits)[0]
+        q_ref, s_ref = oracle.act_quant(bits, "bf16")
+        say(f"quant_gemv_group K={K} x={akind}")
+        packs, refs = zip(*[packed_pair(env, weights(k, n, K)) for k, n in zip(kinds, Ns)])
+        accs = [torch.full((n,), 7, dtype=torch.int32, device="cuda") for n in Ns]
+        ys = tq.tq_quant_gemv_group(x, list(packs), scales, acc=accs)
+        torch.cuda.synchronize()
+        for i, (k, n) in enumerate(zip(kinds, Ns)):
+            acc_ref, y32 = oracle.gemv(refs[i], scales[i], q_ref, s_ref, n)
+            got = accs[i].cpu().numpy()[None, :]
+            np.testing.assert_array_equal(got, acc_ref)
+            check_closed(k, got, q_ref)
+            check_y(ys[i].cpu().numpy()[None, :], y32,
+                    oracle.rescale(acc_ref, scales[i], s_ref, exact=True))
+
+
+@pytest.mark.parametrize("K", [2560, 32768, 32784])
+def test_rmsnorm_quant_gemv_closed_forms(env, K):
+    """The RMSNorm-folded prologue with gamma = 1 on rows of +-1: codes
+    +-127, so the sums are the closed forms; the scale carries the RMS
+    factor (checked against the oracle within one fp32 ulp, as its tests
+    allow)."""
+    torch, tq, oracle = env
+    gbits = workloads.to_bf16_bits(np.ones((1, K), np.float32))[0]
+    gamma = dev_bf16(env, gbits)
+    s_w = np.float32(0.023)
+    for akind in ("all127", "alt127"):
+        bits = act_rows(akind, 1, K)
+        x = dev_bf16(env, bits)[0]
+        q_ref, s_ref = oracle.rmsnorm_act_quant(bits, gbits, 1e-5, "bf16")
+        assert np.all(np.abs(q_ref) == 127)
+        for wkind in W_CONST:
+            say(f"rmsnorm_quant_gemv K={K} W={wkind} x={akind}")
+            p, ref = packed_pair(env, weights(wkind, 68, K))
+            acc = torch.full((68,), 7, dtype=torch.int32, device="cuda")
+            xq = torch.empty(K, dtype=torch.int8, device="cuda")
+            xs = torch.empty(1, dtype=torch.float32, device="cuda")
+            y = tq.tq_rmsnorm_quant_gemv(x, gamma, p, s_w, eps=1e-5, acc=acc, xq=xq, x_scale=xs)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(xq.cpu().numpy(), q_ref[0])
+            sx = xs.cpu().numpy()
+            assert abs(int(sx.view(np.int32)[0]) - int(s_ref.view(np.int32)[0])) <= 1
+            acc_ref = oracle.ternary_matmul(ref, q_ref, 68)
+            got = acc.cpu().numpy()[None, :]
+            np.testing.assert_array_equal(got, acc_ref)
+            check_closed(wkind, got, q_ref)
+            y64 = oracle.rescale(acc_ref, s_w, sx, exact=True)
+            err = np.abs(y.cpu().numpy().astype(np.float64) - y64[0])
+            assert np.all(err <= REL_TOL * np.abs(y64[0]))
