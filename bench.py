@@ -35,7 +35,8 @@ Timing:
     the read ceiling at the same bytes per launch (tq_stream_read over the
     same pool) and each form's fraction of it.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
-    gate/up + relu^2, the small-batch MFMA GEMM (M = 4, 16, 64), the absmean
+    gate/up + relu^2 (2B-4T and 70B-class), the small-batch MFMA GEMM
+    (M = 4, 16, 64), the absmean
     ternarizer, split-KV decode attention and the 30-layer decode-step chain
     (graph-captured).
   * cpu_baseline: the CPU oracle (plain C) on the same step, once on one
@@ -824,6 +825,58 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
                               / us / 1e3 / HBM_PEAK_GBS, 1)}
     log(f"gate_up: {rows['gate_up_relu2_M1_6912x2560']}")
     del pg, pu
+
+    # a4 at the 70B-class MLP: gate and up [28672, 8192] each, 117 MB of
+    # weights per launch (the largest single hot-path launch), int8 row and
+    # fused bf16 quantization, beside the read ceiling at the same bytes
+    N, K = 28672, 8192
+    pg = pool_of(N, K, 1 << 30, 93000)
+    pu = pool_of(N, K, 1 << 30, 93500)
+    xb = workloads.activations_bf16(1, K, seed=94)
+    xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, s = tq.tq_act_quant(xt)
+    xq1 = torch.empty(K, dtype=torch.int8, device=dev)
+    xs1 = torch.empty(1, dtype=torch.float32, device=dev)
+    h = torch.empty(N, dtype=torch.float32, device=dev)
+    wb2 = 2 * weight_bytes(N, K)
+
+    def fg70(st):
+        for r in range(R):
+            i = (st + r) % len(pg)
+            tq.tq_gate_up_relu2(pg[i], 0.024, pu[i], 0.025, q, s, h)
+
+    def fq70(st):
+        for r in range(R):
+            i = (st + r) % len(pg)
+            tq.tq_quant_gate_up_relu2(xt[0], pg[i], 0.024, pu[i], 0.025, h, xq=xq1,
+                                      x_scale=xs1)
+    us_i8 = loop_us(fg70, len(pg))
+    us_fq = loop_us(fq70, len(pg))
+    del pu
+    # one buffer of both matrices' bytes per launch, 12 distinct buffers
+    cat = [torch.empty(wb2, dtype=torch.uint8, device=dev) for _ in range(12)]
+    for c in cat:
+        c.random_(0, 255)
+    sink = torch.zeros(4096, 4, dtype=torch.int32, device=dev)
+
+    def fr70(st):
+        for r in range(R):
+            tq.tq_stream_read(cat[(st + r) % len(cat)], sink)
+    us_rd = loop_us(fr70, len(cat))
+    del pg, cat
+    rows["gate_up_relu2_M1_70b_28672x8192"] = {
+        "weight_bytes": wb2,
+        "int8": {"us_per_launch": round(us_i8, 3),
+                 "weight_GBs": round(wb2 / us_i8 / 1e3, 1),
+                 "pct_hbm_peak": round(100 * wb2 / us_i8 / 1e3 / HBM_PEAK_GBS, 1),
+                 "frac_of_read_ceiling": round(us_rd / us_i8, 3)},
+        "quant_fused": {"us_per_launch": round(us_fq, 3),
+                        "weight_GBs": round(wb2 / us_fq / 1e3, 1),
+                        "pct_hbm_peak": round(100 * wb2 / us_fq / 1e3 / HBM_PEAK_GBS, 1),
+                        "frac_of_read_ceiling": round(us_rd / us_fq, 3)},
+        "read_ceiling_us": round(us_rd, 3),
+        "read_ceiling_pct_hbm_peak": round(100 * wb2 / us_rd / 1e3 / HBM_PEAK_GBS, 1)}
+    log(f"gate_up 70b: {rows['gate_up_relu2_M1_70b_28672x8192']}")
 
     # a5: small-batch GEMM on the int8 matrix cores
     gemm = {}
