@@ -128,6 +128,75 @@ __device__ __forceinline__ void reduce_scatter(float (&val)[N], int lt) {
   }
 }
 
+// Wave reductions by DPP that end in the last lane (row shifts within each
+// 16-lane row, then the two row broadcasts).  For the maximum a lane with no
+// source keeps its own value; for the sum it adds zero.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_keep(float v) {
+  const int x = __float_as_int(v);
+  return __int_as_float(__builtin_amdgcn_update_dpp(x, x, Ctrl, RowMask, 0xf, false));
+}
+
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, RowMask, 0xf, false));
+}
+
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ double dpp_zero(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, Ctrl, RowMask, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), Ctrl, RowMask, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+__device__ __forceinline__ float wave_max_last(float v) {
+  v = fmaxf(v, dpp_keep<0x111, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x112, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x114, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x118, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  return fmaxf(v, dpp_keep<0x143, 0xc>(v));
+}
+
+__device__ __forceinline__ float wave_sum_last(float v) {
+  v += dpp_zero<0x111, 0xf>(v);
+  v += dpp_zero<0x112, 0xf>(v);
+  v += dpp_zero<0x114, 0xf>(v);
+  v += dpp_zero<0x118, 0xf>(v);
+  v += dpp_zero<0x142, 0xa>(v);
+  return v + dpp_zero<0x143, 0xc>(v);
+}
+
+__device__ __forceinline__ double wave_sum_last(double v) {
+  v += dpp_zero<0x111, 0xf>(v);
+  v += dpp_zero<0x112, 0xf>(v);
+  v += dpp_zero<0x114, 0xf>(v);
+  v += dpp_zero<0x118, 0xf>(v);
+  v += dpp_zero<0x142, 0xa>(v);
+  return v + dpp_zero<0x143, 0xc>(v);
+}
+
+// v plus its value in lane (lane ^ OFF), OFF = 8, 16 or 32, without an LDS
+// round trip: a DPP rotate by 8 within each 16-lane row (which is lane ^ 8),
+// or the row-swap instructions of gfx950 (v_permlane16_swap /
+// v_permlane32_swap: called with one value as both operands, the two
+// results hold the two partners of every pair).  Both lanes of a pair get
+// the same sum, bit for bit, as from a shuffle (addition commutes).
+template <int OFF>
+__device__ __forceinline__ float add_lane_xor(float v) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane offset");
+  if constexpr (OFF == 8) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+  } else if constexpr (OFF == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+}
+
 template <int G, int D, int KT>
 __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
   using Sh = AttnShape<G, D, KT>;
@@ -203,10 +272,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
   for (int u = 0; u < kT; ++u) rv[u] = row(a.v, i0 + u * TPW + tw);
   __syncthreads();
 
-  // 2. per-head max and exp-sum over the chunk (fixed reduction order).  The
-  // G heads go through one loop and their wave trees interleave: one head
-  // after another, each tree a chain of dependent cross-lane shuffles, took
-  // about 2.5 us per block whatever the chunk length.
+  // 2. per-head max and exp-sum over the chunk (fixed reduction order): per
+  // thread, then a DPP tree per wave ending in its last lane, then the
+  // waves in order.  The G heads go through one loop and their trees
+  // interleave (one head after another, each tree a chain of dependent LDS
+  // shuffles, took about 2.5 us per block whatever the chunk length).
   float mx[G], sum[G];
   {
     float m[G];
@@ -216,10 +286,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < G; ++j) m[j] = fmaxf(m[j], s_lds[j * chunk + i]);
 #pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1)
-#pragma unroll
-      for (int j = 0; j < G; ++j) m[j] = fmaxf(m[j], __shfl_xor(m[j], off, kWave));
-    if (lane == 0) {
+    for (int j = 0; j < G; ++j) m[j] = wave_max_last(m[j]);
+    if (lane == kWave - 1) {
 #pragma unroll
       for (int j = 0; j < G; ++j) red[wave][j] = m[j];
     }
@@ -244,10 +312,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
         sacc[j] += p;
       }
 #pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1)
-#pragma unroll
-      for (int j = 0; j < G; ++j) sacc[j] += __shfl_xor(sacc[j], off, kWave);
-    if (lane == 0) {
+    for (int j = 0; j < G; ++j) sacc[j] = wave_sum_last(sacc[j]);
+    if (lane == kWave - 1) {
 #pragma unroll
       for (int j = 0; j < G; ++j) red[wave][j] = sacc[j];
     }
@@ -299,12 +365,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
     pv_step(rv2, it + STEP);
   }
   // token slots of a wave (lanes LPT apart), then the waves, in order
+  static_assert(LPT == 8 || LPT == 16, "lanes per token row");
 #pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1)
+  for (int j = 0; j < G; ++j)
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] += __shfl_xor(acc[j][e], off, kWave);
+    for (int e = 0; e < 8; ++e) {
+      float t = acc[j][e];
+      if constexpr (LPT == 8) t = add_lane_xor<8>(t);
+      t = add_lane_xor<16>(t);
+      acc[j][e] = add_lane_xor<32>(t);
+    }
   __syncthreads();  // every wave is done reading the weights
   float *o_red = s_lds;  // [NW][G][D]
   if (tw == 0) {
@@ -335,41 +405,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
     p[0] = mx[j];
     p[1] = sum[j];
   }
-}
-
-// Wave reductions by DPP that end in the last lane (row shifts within each
-// 16-lane row, then the two row broadcasts).  For the maximum a lane with no
-// source keeps its own value; for the sum it adds zero.
-template <int Ctrl, int RowMask>
-__device__ __forceinline__ float dpp_keep(float v) {
-  const int x = __float_as_int(v);
-  return __int_as_float(__builtin_amdgcn_update_dpp(x, x, Ctrl, RowMask, 0xf, false));
-}
-
-template <int Ctrl, int RowMask>
-__device__ __forceinline__ double dpp_zero(double v) {
-  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, Ctrl, RowMask, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), Ctrl, RowMask, 0xf, false);
-  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
-}
-
-__device__ __forceinline__ float wave_max_last(float v) {
-  v = fmaxf(v, dpp_keep<0x111, 0xf>(v));
-  v = fmaxf(v, dpp_keep<0x112, 0xf>(v));
-  v = fmaxf(v, dpp_keep<0x114, 0xf>(v));
-  v = fmaxf(v, dpp_keep<0x118, 0xf>(v));
-  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
-  return fmaxf(v, dpp_keep<0x143, 0xc>(v));
-}
-
-__device__ __forceinline__ double wave_sum_last(double v) {
-  v += dpp_zero<0x111, 0xf>(v);
-  v += dpp_zero<0x112, 0xf>(v);
-  v += dpp_zero<0x114, 0xf>(v);
-  v += dpp_zero<0x118, 0xf>(v);
-  v += dpp_zero<0x142, 0xa>(v);
-  return v + dpp_zero<0x143, 0xc>(v);
 }
 
 // Block (h, slice): out[h, d] for kCombineDims dims d, merging the S <=
@@ -406,7 +441,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
   // denominator with DPP trees that end in the last lane; the weights e and
   // the denominator reach the other waves through LDS.
   if (wave == 0) {
-    const double M = __shfl((double)wave_max_last(mv), kWave - 1, kWave);
+    const double M = (double)__int_as_float(
+        __builtin_amdgcn_readlane(__float_as_int(wave_max_last(mv)), kWave - 1));
     const double e = tid < S ? exp((double)mv - M) : 0.0;
     f[tid] = e;
     const double dsum = wave_sum_last(e * (double)lv);
