@@ -89,16 +89,37 @@ __device__ __forceinline__ int group_sum_to_last(int v) {
   return v;
 }
 
+// All-reduce over the wave with no LDS round trip, result in every lane:
+// the two halves, then the two rows of each half, exchanged by gfx950's
+// v_permlane32_swap / v_permlane16_swap (called with one value as both
+// operands, the two results hold the two partners of every lane pair), then
+// DPP rotates by 8, 4, 2, 1 within each 16-lane row (after rotating by 8,
+// each lane holds lanes {i, i+8}; after 4, {i, i+4, i+8, i+12}; and so on).
+// For an associative, commutative, exact op (max, integer sums) every
+// pairing gives the same result.
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, Op op) {
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = op(h[0], h[1]);
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r[0], r[1]);
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor8, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor4, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor2, 0xf, 0xf, false));
+  return op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor1, 0xf, 0xf, false));
+}
+
 // Float max over the whole wave, result valid in every lane.
 __device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1)
-    v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  return __uint_as_float(wave_allreduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  return (int)wave_allreduce((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 // ---------------------------------------------------------------- act quant
@@ -240,12 +261,62 @@ __device__ __forceinline__ RawPiece<false> scale_piece(const RawPiece<kBf16> &x,
   return u;
 }
 
-// fp64 sum over a wave (xor butterfly: every lane ends with the same value,
-// since each step adds the same two partial sums in either order).
+// The value of lane (lane ^ OFF), one 32-bit word, with no LDS round trip:
+// OFF = 8 is a DPP rotate by 8 within each 16-lane row; OFF = 4 takes
+// lane + 4 in the first and third 4-lane bank of each row and lane - 4 in
+// the others (two DPP shifts, each restricted by the bank mask); OFF = 2
+// and 1 are quad permutations.
+template <int OFF>
+__device__ __forceinline__ uint32_t lane_xor_dpp(uint32_t v) {
+  static_assert(OFF == 8 || OFF == 4 || OFF == 2 || OFF == 1, "DPP lane offset");
+  const int x = (int)v;
+  if constexpr (OFF == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, x, kRowRor8, 0xf, 0xf, false);
+  } else if constexpr (OFF == 4) {
+    const int t = __builtin_amdgcn_update_dpp(x, x, 0x104 /* row_shl:4 */, 0xf, 0x5, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(t, x, 0x114 /* row_shr:4 */, 0xf, 0xa, false);
+  } else if constexpr (OFF == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4e /* quad_perm 2,3,0,1 */, 0xf, 0xf, false);
+  } else {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xb1 /* quad_perm 1,0,3,2 */, 0xf, 0xf, false);
+  }
+}
+
+// fp64 sum over a wave as an xor butterfly (lanes 32, 16, 8, 4, 2, 1 apart):
+// every lane ends with the same value, since each step adds the same two
+// partial sums in either order.  The pairs 32 and 16 apart come from the
+// row-swap instructions, the rest from DPP, each on both halves of the
+// double; no LDS round trip.
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  auto halves = [](double d, uint32_t &lo, uint32_t &hi) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(d);
+    lo = (uint32_t)b;
+    hi = (uint32_t)(b >> 32);
+  };
+  auto join = [](uint32_t lo, uint32_t hi) {
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+  };
+  uint32_t lo, hi;
+  halves(v, lo, hi);
+  {
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    v = join(l[0], h[0]) + join(l[1], h[1]);
+  }
+  halves(v, lo, hi);
+  {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    v = join(l[0], h[0]) + join(l[1], h[1]);
+  }
+  halves(v, lo, hi);
+  v += join(lane_xor_dpp<8>(lo), lane_xor_dpp<8>(hi));
+  halves(v, lo, hi);
+  v += join(lane_xor_dpp<4>(lo), lane_xor_dpp<4>(hi));
+  halves(v, lo, hi);
+  v += join(lane_xor_dpp<2>(lo), lane_xor_dpp<2>(hi));
+  halves(v, lo, hi);
+  return v + join(lane_xor_dpp<1>(lo), lane_xor_dpp<1>(hi));
 }
 
 // The RMS factor, rounded once to fp32: 1 / sqrt(ss / K + eps) in fp64.

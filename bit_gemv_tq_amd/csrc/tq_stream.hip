@@ -44,9 +44,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(
     for (int64_t i = tiles * kTile + threadIdx.x; i < n16; i += kStreamThreads)
       x ^= __builtin_nontemporal_load(p + i);
 #pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] ^= (uint32_t)__shfl_xor((int)x[c], off, kWave);
+  for (int c = 0; c < 4; ++c)
+    x[c] = wave_allreduce(x[c], [](uint32_t a, uint32_t b) { return a ^ b; });
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) wx[wave] = x;
   __syncthreads();
