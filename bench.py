@@ -35,7 +35,8 @@ Timing:
     the read ceiling at the same bytes per launch (tq_stream_read over the
     same pool) and each form's fraction of it.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
-    gate/up + relu^2 (2B-4T and 70B-class), the small-batch MFMA GEMM
+    gate/up + relu^2 (2B-4T and 70B-class), the decode chain (30 2B-4T
+    layers, 8 70B-class layers), the small-batch MFMA GEMM
     (M = 4, 16, 64), the absmean
     ternarizer, split-KV decode attention and the 30-layer decode-step chain
     (graph-captured).
@@ -985,6 +986,42 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
             "launches_per_token": launches * workloads.CHAIN_LAYERS}
         log(f"{key}: {rows[key]}")
         del g, chain
+    del layers
+
+    # a6 at the 70B-class shapes: 8 layers (grouped q/k/v [8192,1024,1024],
+    # o [8192,8192], gate/up [28672,8192], down [8192,28672]; 214 MB of
+    # packed weights per layer, 1.7 GB in all), fused, one graph per step
+    cfg70 = workloads.CHAIN_70B_CONFIG
+    n70 = 8
+    layers = []
+    for l in range(n70):
+        packed, scale = {}, {}
+        for name, (N, K) in workloads.LAYER_70B.items():
+            t = workloads.TENSOR_INDEX[name]
+            w = workloads.ternary_codes_torch(N, K, seed=workloads.seed_for(cfg70, t, l),
+                                              device=dev)
+            packed[name] = tq.tq_pack(w)
+            scale[name] = workloads.tensor_scale(t)
+            del w
+        layers.append(Layer(packed, scale))
+    H70 = workloads.LAYER_70B["q"][1]
+    h0b = workloads.activations_bf16(1, H70, seed=workloads.seed_for(cfg70, 9), outliers=True)
+    h0 = torch.from_numpy(h0b.view(np.int16)).view(torch.bfloat16).to(dev)[0]
+    layer_bytes = sum(weight_bytes(*s) for s in workloads.LAYER_70B.values())
+    total = layer_bytes * n70
+    chain = DecodeChain(layers, dev, fused=True)
+    g = timer.graph(lambda: chain.step(h0))
+    ms = timer.time_graphs([g], 10)
+    rows["decode_chain_8x70b"] = {
+        "layers": n70,
+        "weight_bytes_per_layer": layer_bytes,
+        "us_per_step": round(ms * 1e3, 2),
+        "us_per_layer": round(ms * 1e3 / n70, 2),
+        "weight_GBs": round(total / (ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+        "launches_per_layer": 4}
+    log(f"decode_chain_8x70b: {rows['decode_chain_8x70b']}")
+    del g, chain, layers
     return rows
 
 

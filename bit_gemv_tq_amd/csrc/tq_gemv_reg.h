@@ -26,6 +26,8 @@
 // activation loads are issued first, then the first row's weight loads.
 #pragma once
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -105,13 +107,30 @@ __device__ __forceinline__ int seg_of(const RegSegs &sg, int i, int &start) {
   return q;
 }
 
+// Unrolled selects (q may differ between lanes) of candidates pinned in
+// scalar registers by an empty asm statement: left alone, the compiler turns
+// the selects into a vector load of the argument block indexed by q, and the
+// wait for that load (vmcnt 0) costs every output row a memory round trip
+// (70B-class q/k/v in one launch: 8.4 against 6.9 us for one concatenated
+// matrix of the same bytes).
 template <typename T>
 __device__ __forceinline__ T seg_pick(const T (&v)[kMaxSeg], int q) {
-  T r = v[0];  // unrolled selects: q may differ between lanes
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "scalar-register candidates");
+  using B = typename std::conditional<sizeof(T) == 4, uint32_t, uint64_t>::type;
+  B r = __builtin_bit_cast(B, v[0]);
+  asm volatile("" : "+s"(r));
 #pragma unroll
-  for (int t = 1; t < kMaxSeg; ++t) r = q == t ? v[t] : r;
-  return r;
+  for (int t = 1; t < kMaxSeg; ++t) {
+    B c = __builtin_bit_cast(B, v[t]);
+    asm volatile("" : "+s"(c));
+    r = q == t ? c : r;
+  }
+  return __builtin_bit_cast(T, r);
 }
+
+// Global-memory views of output pointers (see the grouped emit).
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) int32_t gint32;
 
 // Segment q's packed matrix, for the weight loads.  The candidates pass
 // through an empty asm statement that pins them in scalar registers: left
@@ -172,6 +191,14 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
     its = (n4 - 1 - rb0) / row_stride + 1;
   }
 
+  // A row index that is the same in every lane of a wave (teams of 64 or
+  // more lanes), made visibly uniform so that the grouped form's segment
+  // lookups are scalar operations.
+  auto wave_row = [&](int r) {
+    if constexpr (LPR >= kWave) return __builtin_amdgcn_readfirstlane(r);
+    else return r;
+  };
+
   const uint4 *P[NM];
   P[0] = reinterpret_cast<const uint4 *>(g.p0);
   if constexpr (kGate) P[NM - 1] = reinterpret_cast<const uint4 *>(g.p1);
@@ -212,7 +239,7 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
       const uint4 *rp = P[m] + (size_t)row * kp;
       if (!kGate && g.seg.n > 0) {  // grouped: the row's own matrix
         int start;
-        const int q = seg_of(g.seg, row, start);
+        const int q = seg_of(g.seg, wave_row(row), start);
         rp = reinterpret_cast<const uint4 *>(seg_matrix(g.seg, q)) +
              (size_t)(row - start) * kp;
       }
@@ -340,6 +367,25 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[m][j] = group_sum_to_last<GL>(a[m][j]);
     const int i = rbase + team;
+    // The row's outputs: y, acc, scale and row count of its matrix.  In the
+    // grouped form one segment lookup per row serves all four outputs (a
+    // lookup per output, with its selects pinned apart by the asm statements,
+    // made the emit dozens of dependent instructions per output: 2.4 us per
+    // launch).  Stores go through global-memory pointers (a selected pointer
+    // is generic to the compiler, and would give flat stores).
+    gfloat *yo = (gfloat *)g.y;
+    gint32 *ao = (gint32 *)g.acc0;
+    float co = c0;
+    int n4o = n4, io = i;
+    if (!kGate && g.seg.n > 0) {
+      int start;
+      const int q = seg_of(g.seg, wave_row(i), start);
+      n4o = seg_pick(g.seg.end, q) - start;
+      io = i - start;
+      yo = (gfloat *)seg_pick(g.seg.y, q);
+      ao = (gint32 *)seg_pick(g.seg.acc, q);
+      co = seg_pick(g.seg.s, q) * sx;
+    }
     auto emit = [&](int j, int v0, int v1) {
       if (i >= n4) return;
       const int sh = j == 0 ? 0 : (j == 1 ? 2 : 4);
@@ -350,18 +396,10 @@ __global__ __launch_bounds__(BT) void gemv_reg_kernel(RegArgs g) {
         if (g.acc0) g.acc0[n] = t0;
         if (g.acc1) g.acc1[n] = t1;
         g.y[n] = relu2_gate(rescale(t0, c0), rescale(t1, c1));
-      } else if (g.seg.n > 0) {
-        int start;
-        const int q = seg_of(g.seg, i, start);
-        const int n4q = seg_pick(g.seg.end, q) - start;
-        const size_t n = (size_t)j * n4q + (i - start);
-        int32_t *acc = seg_pick(g.seg.acc, q);
-        if (acc) acc[n] = t0;
-        seg_pick(g.seg.y, q)[n] = rescale(t0, seg_pick(g.seg.s, q) * sx);
       } else {
-        const size_t n = (size_t)j * n4 + i;
-        if (g.acc0) g.acc0[n] = t0;
-        g.y[n] = rescale(t0, c0);
+        const size_t n = (size_t)j * n4o + io;
+        if (ao) ao[n] = t0;
+        yo[n] = rescale(t0, co);
       }
     };
     if constexpr (WPT == 1) {

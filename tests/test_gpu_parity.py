@@ -331,7 +331,8 @@ GROUP_CASES = [((2560, 640, 640), 2560, "bf16"),      # 2B-4T q, k, v
                ((4, 8), 40000, "f32"),                # K > 32768: fallback
                ((12, 4), 0, "bf16"),                  # K == 0
                ((1024,), 4608, "bf16"),
-               ((4096, 2048, 2048), 20480, "bf16")]  # rows by dispatch round
+               ((4096, 2048, 2048), 20480, "bf16"),  # rows by dispatch round
+               ((8192, 1024, 1024), 8192, "bf16")]   # 70B-class q, k, v
 
 
 @pytest.mark.parametrize("Ns,K,dtype", GROUP_CASES)

@@ -44,6 +44,21 @@ LAYER_2B4T = {
 }
 TENSOR_INDEX = {name: t for t, name in enumerate(LAYER_2B4T)}
 
+# A 70B-class layer for the decode chain at the large shapes: hidden 8192,
+# intermediate 28672 (the 70B-class shapes above), q/o [8192, 8192] and
+# grouped-query k/v of 8 heads x 128 = 1024 rows.  Same projection names,
+# so TENSOR_INDEX applies.
+LAYER_70B = {
+    "q": (8192, 8192),
+    "k": (1024, 8192),
+    "v": (1024, 8192),
+    "o": (8192, 8192),
+    "gate": (28672, 8192),
+    "up": (28672, 8192),
+    "down": (8192, 28672),
+}
+CHAIN_70B_CONFIG = 7  # seed_for config id of its weights and input
+
 # 8B- and 70B-class M=1 layers, both orientations: (N, K).
 LARGE_SHAPES = {
     "8b_up": (14336, 4096),
