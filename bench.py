@@ -805,6 +805,42 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
         del P3
     rows["gemv3_five_per_byte"] = g3
 
+    # grouped q/k/v (one launch for the three projections that share x),
+    # 2B-4T and 70B-class, against one concatenated matrix of the same bytes
+    grp = {}
+    for tag, Ns, K in (("2b4t_qkv", (2560, 640, 640), 2560),
+                       ("70b_qkv", (8192, 1024, 1024), 8192)):
+        P = [pool_of(N, K, (512 << 20) if N > 2048 else (128 << 20), 81000 + 1000 * c)
+             for c, N in enumerate(Ns)]
+        Cc = pool_of(sum(Ns), K, 1 << 30, 85000)
+        xb = workloads.activations_bf16(1, K, seed=98)
+        xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)[0]
+        ys = [torch.empty(N, dtype=torch.float32, device=dev) for N in Ns]
+        yc = torch.empty(sum(Ns), dtype=torch.float32, device=dev)
+        xq1 = torch.empty(K, dtype=torch.int8, device=dev)
+        xs1 = torch.empty(1, dtype=torch.float32, device=dev)
+        nP = min(len(p) for p in P)
+
+        def fgrp(st, P=P, xt=xt, ys=ys, xq1=xq1, xs1=xs1, nP=nP):
+            for r in range(R):
+                i = (st + r) % nP
+                tq.tq_quant_gemv_group(xt, [p[i] for p in P], [0.02, 0.021, 0.022], ys,
+                                       xq=xq1, x_scale=xs1)
+
+        def fcat(st, Cc=Cc, xt=xt, yc=yc, xq1=xq1, xs1=xs1):
+            for r in range(R):
+                tq.tq_quant_gemv(xt, Cc[(st + r) % len(Cc)], 0.02, yc, xq=xq1, x_scale=xs1)
+        us_g = loop_us(fgrp, nP)
+        us_c = loop_us(fcat, len(Cc))
+        wb = sum(weight_bytes(N, K) for N in Ns)
+        grp[tag] = {"Ns": list(Ns), "K": K, "weight_bytes": wb,
+                    "grouped_us": round(us_g, 3),
+                    "grouped_weight_GBs": round(wb / us_g / 1e3, 1),
+                    "one_matrix_us": round(us_c, 3)}
+        log(f"grouped {tag}: {grp[tag]}")
+        del P, Cc
+    rows["quant_gemv_group_qkv"] = grp
+
     # a4: fused gate/up + relu^2, M = 1 (2B-4T MLP)
     N, K = workloads.INTERMEDIATE, workloads.HIDDEN
     pg = pool_of(N, K, 320 << 20, 91000)
