@@ -199,7 +199,19 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate, int xt) {
   int lpr = 16;
   while ((kp + lpr - 1) / lpr > 8) lpr *= 2;
   const int64_t want_lanes = (int64_t)num_cus * 16 * kWave;
-  if (lpr < 64 && n4 * lpr < want_lanes) lpr = 64;
+  // Narrow teams hold more loads per lane; where they give too few lanes the
+  // teams are widened to 64 lanes -- except in the two-matrix gate form with
+  // a raw (bf16/fp32) row, when 32-lane teams still fill 3/4 to all of the
+  // CUs with one block each: half the blocks quantize the row in their
+  // prologue.  Measured at the 2B-4T MLP, [6912,2560] x 2, fp32 row: 32-lane
+  // teams on 216 blocks 4.24 us against 5.44 us for 64-lane teams on 432
+  // blocks (kernel trace); with an int8 row the 64-lane plan stays faster
+  // (4.3 against 4.5 us).
+  const int64_t narrow_blocks = n4 / (kRegThreads / 32);
+  const bool keep_narrow = gate && xt != kXInt8 && lpr == 32 &&
+                           narrow_blocks * 4 >= (int64_t)num_cus * 3 &&
+                           narrow_blocks <= num_cus;
+  if (lpr < 64 && n4 * lpr < want_lanes && !keep_narrow) lpr = 64;
   pl.lpr = lpr;
   pl.np = (int)((kp + lpr - 1) / lpr);
   pl.exact = (int64_t)pl.np * lpr == kp;
