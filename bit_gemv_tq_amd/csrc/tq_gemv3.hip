@@ -169,6 +169,10 @@ __global__ __launch_bounds__(reg_block_threads(LPR)) void gemv3_kernel(Gemv3Args
   consume(wa, rb0);
   for (int it = 1; it < its; ++it) {
     issue(wa, rb0 + it * row_stride);
+    // Every load of the row ahead of its decode (left alone, the scheduler
+    // waits for the first pieces after issuing two loads and spreads the
+    // rest of the row's loads over the decode).
+    __builtin_amdgcn_sched_barrier(0);
     consume(wa, rb0 + it * row_stride);
   }
 }
