@@ -153,6 +153,13 @@ __global__ __launch_bounds__(MAXW *kWave) void gemm_quad_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < RG; ++q) acc[m][q] = v4i{0, 0, 0, 0};
 
+  // The epilogue's activation scale for this thread's first output slot,
+  // loaded now: its latency hides behind the main loop instead of following
+  // the final barrier.
+  float sx_first = 0.0f;
+  if ((int)threadIdx.x < RG * 64)
+    sx_first = g.x_scale[min(m0 + (int)threadIdx.x / (4 * RG), M - 1)];
+
   const int groups = (K + kGroup - 1) / kGroup;
   for (int g0 = wave * NQ; g0 < groups; g0 += W * NQ) {
     // 1. Every load of the pass.  Past K (a ragged last group, or groups past
@@ -230,8 +237,7 @@ __global__ __launch_bounds__(MAXW *kWave) void gemm_quad_kernel(GemmArgs g) {
   __syncthreads();
   // 5. Cross-wave sums (exact) and the epilogue.  Thread t: packed row
   // i0 + 4q + aa, activation row m0 + mm; consecutive threads, consecutive
-  // output columns.  The scale is read once, before the stores (y may alias
-  // it).
+  // output columns.  The scale is read before the stores (y may alias it).
   const size_t N = (size_t)n4 * 4;
   for (int t = threadIdx.x; t < RG * 64; t += blockDim.x) {
     const int aa = t & 3, q = (t >> 2) % RG, mm = t / (4 * RG);
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(MAXW *kWave) void gemm_quad_kernel(GemmArgs g) {
     }
     const int p = i0 + 4 * q + aa, m = m0 + mm;
     if (p >= n4 || m >= M) continue;
-    const float sx = g.x_scale[m];
+    const float sx = t == (int)threadIdx.x ? sx_first : g.x_scale[m];
     const float c0 = g.s0 * sx, c1 = g.s1 * sx;
     const size_t o = (size_t)m * N + p;
 #pragma unroll
