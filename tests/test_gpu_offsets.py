@@ -1,0 +1,223 @@
+"""GPU parity past 4 GiB of packed weights.
+
+The C ABI accepts up to 2^31 - 1 packed rows of up to 131072 bytes, so byte
+offsets into one weight matrix can pass 2^31 and 2^32.  These cases put the
+packed rows a kernel reads on both sides of those offsets and compare the
+outputs of sampled rows (first, middle, the rows that straddle 2^31 and 2^32
+bytes, last) against the CPU oracle: int32 sums bit-exact, fp32 outputs
+bit-exact against the oracle's fixed-order rescale.
+
+The matrices (4.3 GB each) are filled on the GPU with random valid packed
+bytes: the byte values come from the oracle's own packing of every
+combination of codes, drawn uniformly.  The oracle then sees only the
+sampled packed rows, as a small packed matrix: packed row i of the planar
+layout holds output rows j * (N/4) + i (j = 0..3; j * ceil(N/5) + i for
+five weights per byte), so sub-matrix row s stands for those of S[s].
+"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+K_REG = 16384                       # register-resident GEMV and the MFMA GEMM
+N4_BIG = (1 << 32) // K_REG + 64    # 262208 packed rows: 4,296,015,872 bytes
+K_LONG = 65536                      # the LDS-staged GEMV (K > 32768)
+N4_LONG = (1 << 32) // K_LONG + 64  # 65600 packed rows: 4,299,161,600 bytes
+N4_GATE = (1 << 31) // K_REG + 32   # 131104 rows per matrix: past 2^31 each
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import bit_gemv_tq_amd as tq
+    import oracle
+    return torch, tq, oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def sample_rows(n_rows, K):
+    """Packed rows around byte offsets 2^31 and 2^32, plus the ends."""
+    s = {0, 1, n_rows // 2, n_rows - 2, n_rows - 1}
+    for off in (1 << 31, 1 << 32):
+        r = off // K
+        s |= {r - 1, r, r + 1}
+    return np.array(sorted(x for x in s if 0 <= x < n_rows), np.int64)
+
+
+def valid_bytes(oracle, per_byte):
+    """Every packed byte value the oracle produces (81 or 243 of them)."""
+    combos = np.array(list(itertools.product((-1, 0, 1), repeat=per_byte)),
+                      np.int8).T.copy()  # [per_byte, combos]: one column each
+    if per_byte == 4:
+        b = oracle.pack(combos)
+    else:
+        b = oracle.pack3(combos)
+    assert b.shape == (1, combos.shape[1])
+    vals = np.unique(b[0])
+    assert vals.size == combos.shape[1]
+    return vals
+
+
+def random_packed(env, rows, K, lut, seed):
+    """[rows, K] uint8 on the GPU, each byte drawn uniformly from lut."""
+    torch, _, _ = env
+    out = torch.empty(rows, K, dtype=torch.uint8, device="cuda")
+    lut_d = torch.from_numpy(lut.astype(np.uint8)).cuda()
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    step = max(1, (32 << 20) // K)
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        idx = torch.randint(0, lut.size, (r1 - r0, K), generator=g, device="cuda")
+        out[r0:r1] = lut_d[idx]
+    return out
+
+
+def quantized_rows(env, M, K, seed):
+    torch, tq, oracle = env
+    xb = workloads.activations_bf16(M, K, seed=seed, outliers=True)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda().reshape(M, K)
+    xq, xs = tq.tq_act_quant(x)
+    q_ref, s_ref = oracle.act_quant(xb.reshape(M, K), "bf16")
+    np.testing.assert_array_equal(xq.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    return x, xq, xs, q_ref, s_ref
+
+
+def out_index(rows, n_rows, per_byte):
+    """Output rows of packed rows `rows`, in the oracle sub-matrix's order."""
+    return np.concatenate([j * n_rows + rows for j in range(per_byte)])
+
+
+def check(acc_gpu, y_gpu, acc_ref, y_ref):
+    np.testing.assert_array_equal(acc_gpu, acc_ref)
+    np.testing.assert_array_equal(y_gpu.view(np.uint32), y_ref.view(np.uint32))
+
+
+def free(torch):
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_two_bit_past_4gib(env):
+    """tq_gemv, tq_quant_gemv (bf16 row) and tq_gemm_small (M = 4, matrix
+    cores) on one 4.3 GB matrix, K = 16384."""
+    torch, tq, oracle = env
+    n4, K = N4_BIG, K_REG
+    N = 4 * n4
+    say(f"two-bit past 4 GiB: packed [{n4}, {K}] = {n4 * K} bytes")
+    packed = random_packed(env, n4, K, valid_bytes(oracle, 4), seed=41)
+    rows = sample_rows(n4, K)
+    sub = packed[torch.from_numpy(rows).cuda()].cpu().numpy()
+    idx = out_index(rows, n4, 4)
+    s_w = np.float32(0.021)
+
+    x, xq, xs, q_ref, s_ref = quantized_rows(env, 4, K, seed=43)
+    acc_ref = oracle.ternary_matmul(sub, q_ref, 4 * rows.size)
+    y_ref = oracle.rescale(acc_ref, s_w, s_ref)
+
+    say("  tq_gemv")
+    acc = torch.empty(N, dtype=torch.int32, device="cuda")
+    y = tq.tq_gemv(packed, s_w, xq[0], xs[:1], acc=acc)
+    torch.cuda.synchronize()
+    check(acc.cpu().numpy()[idx], y.cpu().numpy()[idx], acc_ref[0], y_ref[0])
+
+    say("  tq_quant_gemv (bf16 row)")
+    acc.fill_(7)
+    y = tq.tq_quant_gemv(x[0], packed, s_w, acc=acc)
+    torch.cuda.synchronize()
+    check(acc.cpu().numpy()[idx], y.cpu().numpy()[idx], acc_ref[0], y_ref[0])
+    del acc, y
+
+    say("  tq_gemm_small M = 4")
+    acc4 = torch.empty(4, N, dtype=torch.int32, device="cuda")
+    y4 = tq.tq_gemm_small(packed, s_w, xq, xs, acc=acc4)
+    torch.cuda.synchronize()
+    check(acc4.cpu().numpy()[:, idx], y4.cpu().numpy()[:, idx], acc_ref, y_ref)
+    del packed, acc4, y4
+    free(torch)
+
+
+def test_two_bit_long_rows_past_4gib(env):
+    """tq_gemv with K = 65536 (activations in LDS) on a 4.3 GB matrix."""
+    torch, tq, oracle = env
+    n4, K = N4_LONG, K_LONG
+    say(f"two-bit long rows past 4 GiB: packed [{n4}, {K}] = {n4 * K} bytes")
+    packed = random_packed(env, n4, K, valid_bytes(oracle, 4), seed=47)
+    rows = sample_rows(n4, K)
+    sub = packed[torch.from_numpy(rows).cuda()].cpu().numpy()
+    idx = out_index(rows, n4, 4)
+    s_w = np.float32(0.017)
+    _, xq, xs, q_ref, s_ref = quantized_rows(env, 1, K, seed=53)
+    acc_ref = oracle.ternary_matmul(sub, q_ref, 4 * rows.size)
+    y_ref = oracle.rescale(acc_ref, s_w, s_ref)
+    acc = torch.empty(4 * n4, dtype=torch.int32, device="cuda")
+    y = tq.tq_gemv(packed, s_w, xq[0], xs, acc=acc)
+    torch.cuda.synchronize()
+    check(acc.cpu().numpy()[idx], y.cpu().numpy()[idx], acc_ref[0], y_ref[0])
+    del packed, acc, y
+    free(torch)
+
+
+def test_gate_up_past_2gib_each(env):
+    """tq_gate_up_relu2 at M = 1 and M = 4 with two 2.1 GB matrices."""
+    torch, tq, oracle = env
+    n4, K = N4_GATE, K_REG
+    N = 4 * n4
+    say(f"gate/up past 2 GiB each: 2 x packed [{n4}, {K}] = {n4 * K} bytes")
+    lut = valid_bytes(oracle, 4)
+    pg = random_packed(env, n4, K, lut, seed=59)
+    pu = random_packed(env, n4, K, lut, seed=61)
+    rows = sample_rows(n4, K)
+    rows_d = torch.from_numpy(rows).cuda()
+    sub_g, sub_u = pg[rows_d].cpu().numpy(), pu[rows_d].cpu().numpy()
+    idx = out_index(rows, n4, 4)
+    s_g, s_u = np.float32(0.023), np.float32(0.029)
+    _, xq, xs, q_ref, s_ref = quantized_rows(env, 4, K, seed=67)
+    ag, au, h_ref = oracle.gate_up_relu2(sub_g, s_g, sub_u, s_u, q_ref, s_ref, 4 * rows.size)
+    for M in (1, 4):
+        say(f"  tq_gate_up_relu2 M = {M}")
+        acc_g = torch.empty(M, N, dtype=torch.int32, device="cuda")
+        acc_u = torch.empty(M, N, dtype=torch.int32, device="cuda")
+        h = tq.tq_gate_up_relu2(pg, s_g, pu, s_u, xq[:M], xs[:M],
+                                acc_gate=acc_g, acc_up=acc_u)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc_g.cpu().numpy()[:, idx], ag[:M])
+        np.testing.assert_array_equal(acc_u.cpu().numpy()[:, idx], au[:M])
+        np.testing.assert_array_equal(h.reshape(M, N).cpu().numpy()[:, idx].view(np.uint32),
+                                      h_ref[:M].view(np.uint32))
+        del acc_g, acc_u, h
+    del pg, pu
+    free(torch)
+
+
+def test_five_per_byte_past_4gib(env):
+    """tq_gemv3 on a 4.3 GB five-per-byte matrix, K = 16384."""
+    torch, tq, oracle = env
+    n5, K = N4_BIG, K_REG
+    N = 5 * n5
+    say(f"five per byte past 4 GiB: packed [{n5}, {K}] = {n5 * K} bytes")
+    packed = random_packed(env, n5, K, valid_bytes(oracle, 5), seed=71)
+    rows = sample_rows(n5, K)
+    sub = packed[torch.from_numpy(rows).cuda()].cpu().numpy()
+    idx = out_index(rows, n5, 5)
+    codes = oracle.unpack3(sub, 5 * rows.size)  # [5 * len(rows), K]
+    s_w = np.float32(0.019)
+    _, xq, xs, q_ref, s_ref = quantized_rows(env, 1, K, seed=73)
+    # exact integer sums of the sampled rows (codes and q are small ints)
+    acc_ref = (codes.astype(np.int64) @ q_ref[0].astype(np.int64)).astype(np.int32)
+    y_ref = oracle.rescale(acc_ref, s_w, s_ref)[0]
+    acc = torch.empty(N, dtype=torch.int32, device="cuda")
+    y = tq.tq_gemv3(packed, s_w, xq[0], xs, N, acc=acc)
+    torch.cuda.synchronize()
+    check(acc.cpu().numpy()[idx], y.cpu().numpy()[idx], acc_ref, y_ref)
+    del packed, acc, y
+    free(torch)
