@@ -108,8 +108,9 @@ def free(torch):
 
 
 def test_two_bit_past_4gib(env):
-    """tq_gemv, tq_quant_gemv (bf16 row) and tq_gemm_small (M = 4, matrix
-    cores) on one 4.3 GB matrix, K = 16384."""
+    """tq_gemv, tq_quant_gemv (bf16 row), tq_quant_gemv_group,
+    tq_rmsnorm_quant_gemv and tq_gemm_small (M = 4, matrix cores) on one
+    4.3 GB matrix, K = 16384."""
     torch, tq, oracle = env
     n4, K = N4_BIG, K_REG
     N = 4 * n4
@@ -135,6 +136,40 @@ def test_two_bit_past_4gib(env):
     y = tq.tq_quant_gemv(x[0], packed, s_w, acc=acc)
     torch.cuda.synchronize()
     check(acc.cpu().numpy()[idx], y.cpu().numpy()[idx], acc_ref[0], y_ref[0])
+    del y
+
+    say("  tq_quant_gemv_group (a small matrix, then the big one)")
+    small = random_packed(env, 64, K, valid_bytes(oracle, 4), seed=42)
+    ys = [torch.empty(256, device="cuda"), torch.empty(N, device="cuda")]
+    accs = [torch.full((256,), 7, dtype=torch.int32, device="cuda"), acc]
+    tq.tq_quant_gemv_group(x[0], [small, packed], [np.float32(0.5), s_w], y=ys, acc=accs)
+    torch.cuda.synchronize()
+    acc_s = oracle.ternary_matmul(small.cpu().numpy(), q_ref[:1], 256)
+    check(accs[0].cpu().numpy(), ys[0].cpu().numpy(), acc_s[0],
+          oracle.rescale(acc_s, np.float32(0.5), s_ref[:1])[0])
+    check(acc.cpu().numpy()[idx], ys[1].cpu().numpy()[idx], acc_ref[0], y_ref[0])
+    del small, ys, accs
+
+    say("  tq_rmsnorm_quant_gemv (bf16 row)")
+    rng = np.random.default_rng(44)
+    gamma = (1.0 + 0.25 * rng.standard_normal(K)).astype(np.float32)
+    gbits = (gamma.view(np.uint32) >> 16).astype(np.uint16)
+    xbits = x[0].cpu().view(torch.int16).numpy().view(np.uint16)
+    q_r, s_r = oracle.rmsnorm_act_quant(xbits.reshape(1, K), gbits, 1e-5, "bf16")
+    xq_r = torch.empty(K, dtype=torch.int8, device="cuda")
+    xs_r = torch.empty(1, dtype=torch.float32, device="cuda")
+    acc.fill_(7)
+    y = tq.tq_rmsnorm_quant_gemv(x[0], torch.from_numpy(gbits.view(np.int16)).view(torch.bfloat16).cuda(),
+                                 packed, s_w, eps=1e-5, acc=acc, xq=xq_r, x_scale=xs_r)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(xq_r.cpu().numpy(), q_r[0])
+    s_gpu = xs_r.cpu().numpy()
+    assert abs(float(s_gpu[0]) - float(s_r[0])) <= np.spacing(s_r[0])  # one ulp
+    acc_r = oracle.ternary_matmul(sub, q_r, 4 * rows.size)[0]
+    np.testing.assert_array_equal(acc.cpu().numpy()[idx], acc_r)
+    # y is the fixed-order fp32 rescale with the scale the call produced
+    y_r = oracle.rescale(acc_r, s_w, s_gpu)[0]
+    np.testing.assert_array_equal(y.cpu().numpy()[idx].view(np.uint32), y_r.view(np.uint32))
     del acc, y
 
     say("  tq_gemm_small M = 4")
