@@ -256,3 +256,38 @@ def test_five_per_byte_past_4gib(env):
     check(acc.cpu().numpy()[idx], y.cpu().numpy()[idx], acc_ref, y_ref)
     del packed, acc, y
     free(torch)
+
+
+def test_attention_past_4gib(env):
+    """tq_attn_decode over a KV cache of 4.56 GB per tensor: L = 131072
+    tokens, 136 KV heads of D = 128 (one query head each), so the rows of
+    the last tokens sit past byte offset 2^32.  Sampled heads against the
+    fp64 oracle within the attention tests' derived per-element bound."""
+    torch, tq, oracle = env
+    import test_gpu_attn as ta
+    L, Hkv, D = 131072, 136, 128
+    H = Hkv
+    say(f"attention past 4 GiB: k/v [{L}, {Hkv}, {D}] bf16 = {L * Hkv * D * 2} bytes each")
+    g = torch.Generator(device="cuda").manual_seed(79)
+    k = torch.empty(L, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty(L, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    step = 4096
+    for t0 in range(0, L, step):
+        k[t0:t0 + step] = torch.randn(step, Hkv, D, generator=g, device="cuda").to(torch.bfloat16)
+        v[t0:t0 + step] = torch.randn(step, Hkv, D, generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn(H, D, generator=g, device="cuda")
+    ws = tq.attn_workspace(H, D, L, q.device)
+    out = tq.tq_attn_decode(q, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    scale = np.float32(1.0 / np.sqrt(D))
+    for h in (0, 67, H - 1):
+        kh = k[:, h, :].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)[:, None, :]
+        vh = v[:, h, :].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)[:, None, :]
+        qh = q[h:h + 1].cpu().numpy()
+        ref = oracle.attn_decode(qh, kh, vh, scale)
+        tol = ta.bound(qh, kh, vh, ref, scale, L, 1, D)
+        err = np.abs(got[h:h + 1] - ref)
+        assert np.all(err <= tol), (h, float(np.max(err / tol)))
+    del k, v, q, ws, out
+    free(torch)
