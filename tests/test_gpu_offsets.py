@@ -291,3 +291,31 @@ def test_attention_past_4gib(env):
         assert np.all(err <= tol), (h, float(np.max(err / tol)))
     del k, v, q, ws, out
     free(torch)
+
+
+@pytest.mark.parametrize("per_byte", [4, 5])
+def test_pack_past_4gib(env, per_byte):
+    """tq_pack / tq_pack3 writing a 4.3 GB packed matrix (from 17 / 21 GB of
+    int8 codes): sampled packed rows equal the oracle's packing of their
+    code rows."""
+    torch, tq, oracle = env
+    n_rows, K = N4_BIG, K_REG
+    N = per_byte * n_rows
+    say(f"pack ({per_byte} per byte) past 4 GiB: codes [{N}, {K}], packed [{n_rows}, {K}]")
+    g = torch.Generator(device="cuda").manual_seed(83 + per_byte)
+    w = torch.empty(N, K, dtype=torch.int8, device="cuda")
+    step = (256 << 20) // K
+    for r0 in range(0, N, step):
+        r1 = min(N, r0 + step)
+        w[r0:r1] = torch.randint(-1, 2, (r1 - r0, K), generator=g, device="cuda",
+                                 dtype=torch.int8)
+    packed = tq.tq_pack(w) if per_byte == 4 else tq.tq_pack3(w)
+    torch.cuda.synchronize()
+    assert packed.shape == (n_rows, K)
+    rows = sample_rows(n_rows, K)
+    idx = torch.from_numpy(out_index(rows, n_rows, per_byte)).cuda()
+    codes = w[idx].cpu().numpy()  # [per_byte * len(rows), K], sub-matrix order
+    ref = oracle.pack(codes) if per_byte == 4 else oracle.pack3(codes)
+    np.testing.assert_array_equal(packed[torch.from_numpy(rows).cuda()].cpu().numpy(), ref)
+    del w, packed
+    free(torch)
