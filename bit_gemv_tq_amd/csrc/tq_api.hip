@@ -19,7 +19,9 @@ tq_status current_device(DeviceInfo *info) {
     (void)hipGetLastError();  // do not leave our probe's error behind
     return TQ_ERR_DEVICE;
   }
-  int cus = g_num_cus[dev].load(std::memory_order_relaxed);
+  // The CU count is published last (release), so a thread that sees it
+  // (acquire) also sees the shared-memory size stored before it.
+  int cus = g_num_cus[dev].load(std::memory_order_acquire);
   int shm = g_max_shared[dev].load(std::memory_order_relaxed);
   if (cus <= 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
@@ -34,7 +36,7 @@ tq_status current_device(DeviceInfo *info) {
       shm = 65536;
     }
     g_max_shared[dev].store(shm, std::memory_order_relaxed);
-    g_num_cus[dev].store(cus, std::memory_order_relaxed);
+    g_num_cus[dev].store(cus, std::memory_order_release);
   }
   info->device = dev;
   info->num_cus = cus;
