@@ -285,10 +285,13 @@ def test_gemm_small_zero_k(env):
 # ------------------------------------------------------------------ fused
 # (8192, 28672) and (8400, 20000) take the rows-by-dispatch-round mapping of
 # the bf16 form on a 256-CU part (the second: rounds of unequal row counts,
-# pieces past the row end).
+# pieces past the row end).  (32776, 16400): the fp32 row's two 256-lane
+# teams per block walk up to 9 rows each, so their per-row sum slots are
+# reused (more than 8 rows) across the periodic barrier.
 FUSED_SHAPES = [(4, 16), (12, 48), (100, 1008), (36, 2064), (2560, 2560),
                 (6912, 2560), (2560, 6912), (8, 32768), (4, 32784), (28, 16384),
-                (28672, 8192), (8192, 28672), (8400, 20000), (14336, 4096)]
+                (28672, 8192), (8192, 28672), (8400, 20000), (14336, 4096),
+                (32776, 16400)]
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)
