@@ -386,8 +386,10 @@ def test_quant_gemv_group(env, Ns, K, dtype):
                                           ysu[i].cpu().numpy().view(np.uint32))
 
 
+# (16400, 20480): two 256-lane teams per block walk up to 9 rows of both
+# matrices, reusing their per-row sum slots across the periodic barrier.
 @pytest.mark.parametrize("N,K", [(6912, 2560), (20, 48), (1028, 4608), (256, 28672),
-                                 (8, 40000)])
+                                 (8, 40000), (16400, 20480)])
 def test_quant_gate_up_relu2(env, N, K):
     torch, tq, oracle = env
     say(f"quant_gate_up N={N} K={K}")
