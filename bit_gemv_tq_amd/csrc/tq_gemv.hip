@@ -223,7 +223,9 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate, int xt) {
   // took 12.7 / 11.1 us with the bf16 / int8 row against 13.5 / 11.4 us for
   // 2 two-team blocks and 14.2 / 12.3 us for 4 one-team blocks); the
   // two-plane gate kernel holds more registers, 2 per CU; the 512-thread
-  // fp32 and RMSNorm forms 2 and 1 (what their registers allow).
+  // fp32 and RMSNorm forms 2 and 1 (what their registers allow).  The
+  // launcher lowers a persistent grid further where the compiled kernel
+  // fits fewer blocks (launch_resident).
   const int per_cu = bt == 512 ? (gate || xt_rms(xt) ? 1 : 2) : (gate ? 2 : 3);
   const int64_t cap = (int64_t)num_cus * per_cu;
   // One row per team when that takes at most one more block per CU than
@@ -232,8 +234,10 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate, int xt) {
   // against 5.4 us with 896 blocks of one row per team).
   const bool one_round = bt == kRegThreads && !gate &&
                          blocks <= (int64_t)num_cus * (per_cu + 1);
-  if (blocks > cap && !one_round) blocks = cap;
+  pl.persistent = blocks > cap && !one_round;
+  if (pl.persistent) blocks = cap;
   pl.blocks = (int)(blocks < 1 ? 1 : blocks);
+  pl.cus = num_cus;
   // Rows by dispatch round, for one-team blocks that quantize a bf16 row in
   // the prologue.  The dispatcher places blocks breadth first (block b on a
   // CU in round b / CUs), and on MI355X the second and third block of a CU

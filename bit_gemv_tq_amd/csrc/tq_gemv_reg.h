@@ -26,6 +26,7 @@
 // activation loads are issued first, then the first row's weight loads.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "tq_device.h"
@@ -499,7 +500,41 @@ struct RegPlan {
   int lpr, np, blocks;
   bool exact;
   int round_cus, round_end0, round_end1;  // rows by dispatch round (0: off)
+  bool persistent;  // blocks = resident blocks per CU x CUs, rows walked
+  int cus;
 };
+
+// Launch of a persistent grid, capped at the blocks of this kernel that one
+// CU can hold (asked of the runtime once per kernel and cached in `occ`):
+// the planner's blocks per CU assume a register count that a few forms
+// exceed (the RMSNorm prologue with 128-lane teams at 7-8 pieces per lane,
+// the fp32 row with two 256-lane teams at 8 pieces), and the blocks beyond
+// the resident ones would run as a second wave (measured on MI355X: the
+// RMSNorm form at [16384,14336] 13.7 against 15.7 us, the fp32 row at
+// [8192,30720] 14.4 against 17.2 us).  A capped grid walks its rows evenly
+// (no split by round).
+template <typename K>
+tq_status launch_resident(K kernel, std::atomic<int> &occ, const RegPlan &pl, dim3 block,
+                          hipStream_t s, const RegArgs &args) {
+  int blocks = pl.blocks;
+  RegArgs a = args;
+  if (pl.persistent) {
+    int n = occ.load(std::memory_order_relaxed);
+    if (n == 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, (int)block.x, 0) !=
+              hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        n = -1;  // unknown: keep the plan
+      }
+      occ.store(n, std::memory_order_relaxed);
+    }
+    if (n > 0 && (int64_t)blocks > (int64_t)n * pl.cus) {
+      blocks = n * pl.cus;
+      a.round_cus = 0;
+    }
+  }
+  return launch(kernel, dim3(blocks), block, 0, s, a);
+}
 
 template <int LPR>
 tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
@@ -509,17 +544,26 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
   (pl.exact ? gemv_reg_kernel<LPR, NPV, true, GATE, XT, gemv_block_threads(LPR, XT)>  \
             : gemv_reg_kernel<LPR, NPV, false, GATE, XT, gemv_block_threads(LPR, XT)>)
 
+// One case: the instance's launch, with its resident-block count cached per
+// exact/ragged form.
+#define TQ_REG_NP_CASE(LPR, NPV, GATE, XT)                                      \
+  case NPV: {                                                                  \
+    static std::atomic<int> occ[2];                                            \
+    return launch_resident(TQ_REG_KERNEL(LPR, NPV, GATE, XT), occ[pl.exact ? 1 : 0], \
+                           pl, block, s, a);                                   \
+  }
+
 #define TQ_REG_NP_CASES(LPR, GATE, XT)                                         \
   const dim3 block(gemv_block_threads(LPR, XT));                               \
   switch (pl.np) {                                                             \
-    case 1: return launch(TQ_REG_KERNEL(LPR, 1, GATE, XT), grid, block, 0, s, a); \
-    case 2: return launch(TQ_REG_KERNEL(LPR, 2, GATE, XT), grid, block, 0, s, a); \
-    case 3: return launch(TQ_REG_KERNEL(LPR, 3, GATE, XT), grid, block, 0, s, a); \
-    case 4: return launch(TQ_REG_KERNEL(LPR, 4, GATE, XT), grid, block, 0, s, a); \
-    case 5: return launch(TQ_REG_KERNEL(LPR, 5, GATE, XT), grid, block, 0, s, a); \
-    case 6: return launch(TQ_REG_KERNEL(LPR, 6, GATE, XT), grid, block, 0, s, a); \
-    case 7: return launch(TQ_REG_KERNEL(LPR, 7, GATE, XT), grid, block, 0, s, a); \
-    case 8: return launch(TQ_REG_KERNEL(LPR, 8, GATE, XT), grid, block, 0, s, a); \
+    TQ_REG_NP_CASE(LPR, 1, GATE, XT)                                           \
+    TQ_REG_NP_CASE(LPR, 2, GATE, XT)                                           \
+    TQ_REG_NP_CASE(LPR, 3, GATE, XT)                                           \
+    TQ_REG_NP_CASE(LPR, 4, GATE, XT)                                           \
+    TQ_REG_NP_CASE(LPR, 5, GATE, XT)                                           \
+    TQ_REG_NP_CASE(LPR, 6, GATE, XT)                                           \
+    TQ_REG_NP_CASE(LPR, 7, GATE, XT)                                           \
+    TQ_REG_NP_CASE(LPR, 8, GATE, XT)                                           \
   }                                                                            \
   return TQ_ERR_LAUNCH;
 
@@ -546,7 +590,6 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
   template <>                                                                  \
   tq_status launch_reg_part<LPR, GATE>(const RegPlan &pl, int xt,              \
                                        const RegArgs &a, hipStream_t s) {      \
-    const dim3 grid(pl.blocks);                                                \
     TQ_REG_XT_CASES(LPR, GATE)                                                 \
   }
 
@@ -554,7 +597,6 @@ tq_status launch_reg(const RegPlan &pl, bool gate, int xt, const RegArgs &a,
   template <>                                                                  \
   tq_status launch_reg_part<LPR, false>(const RegPlan &pl, int xt,             \
                                         const RegArgs &a, hipStream_t s) {     \
-    const dim3 grid(pl.blocks);                                                \
     TQ_REG_XT_CASES_RMS(LPR)                                                   \
   }
 

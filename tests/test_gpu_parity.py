@@ -287,11 +287,13 @@ def test_gemm_small_zero_k(env):
 # the bf16 form on a 256-CU part (the second: rounds of unequal row counts,
 # pieces past the row end).  (32776, 16400): the fp32 row's two 256-lane
 # teams per block walk up to 9 rows each, so their per-row sum slots are
-# reused (more than 8 rows) across the periodic barrier.
+# reused (more than 8 rows) across the periodic barrier.  (8192, 30720): the
+# fp32 form's persistent grid is capped at the one block per CU its
+# registers allow.
 FUSED_SHAPES = [(4, 16), (12, 48), (100, 1008), (36, 2064), (2560, 2560),
                 (6912, 2560), (2560, 6912), (8, 32768), (4, 32784), (28, 16384),
                 (28672, 8192), (8192, 28672), (8400, 20000), (14336, 4096),
-                (32776, 16400)]
+                (32776, 16400), (8192, 30720)]
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)

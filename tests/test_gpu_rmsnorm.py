@@ -93,9 +93,10 @@ def test_rmsnorm_act_quant(env, M, K, dtype):
 # (N, K): 2B-4T o_proj and down, the 70B-class down shape, ragged and tiny
 # rows, K past the single-pass limit, N = 0, and (20480, 20480), where each
 # 256-lane team (two per block) walks 10 rows, so its per-row sum slots are
-# reused across the periodic barrier
+# reused across the periodic barrier, and (16384, 14336), whose persistent
+# grid is capped at the two blocks per CU the 128-lane form's registers allow
 SHAPES = [(2560, 2560), (2560, 6912), (8192, 28672), (20, 48), (100, 4112),
-          (4, 16), (8, 32784), (0, 2560), (20480, 20480)]
+          (4, 16), (8, 32784), (0, 2560), (20480, 20480), (16384, 14336)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
