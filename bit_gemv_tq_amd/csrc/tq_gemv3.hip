@@ -183,10 +183,12 @@ struct Plan3 {
 };
 
 // As the two-bit kernel's plan: the narrowest team with at most 8 pieces per
-// lane, 64-lane teams when rows are few; persistent grids of 3 blocks per CU
-// (4 for 512-thread blocks: this kernel is VALU bound, and more resident
-// waves hide its loads better -- measured 15.9 vs 16.8 us at [8192,28672],
-// 13.7 vs 15.8 us at [28672,8192] against 2 per CU).
+// lane, 64-lane teams when rows are few; grids of at most 3 blocks per CU,
+// 4 for 512-thread blocks.  At 5-8 pieces per lane a CU holds only 2 of the
+// 512-thread blocks (86-114 VGPRs), so a grid of one row per team beyond
+// that runs as a second wave of blocks; measured on MI355X it still beat a
+// grid of 2 blocks per CU whose teams walk two rows (15.9 against 16.8 us
+// at [8192,28672]: 820 blocks of one row per team).
 Plan3 plan3(int64_t n5, int64_t kp, int num_cus) {
   Plan3 pl{};
   int lpr = 16;
