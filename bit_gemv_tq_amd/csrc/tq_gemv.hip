@@ -226,7 +226,13 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate, int xt) {
   // fp32 and RMSNorm forms 2 and 1 (what their registers allow).  The
   // launcher lowers a persistent grid further where the compiled kernel
   // fits fewer blocks (launch_resident).
-  const int per_cu = bt == 512 ? (gate || xt_rms(xt) ? 1 : 2) : (gate ? 2 : 3);
+  // The gate form with short rows (at most 4 pieces per lane) takes 3
+  // blocks per CU: measured on MI355X, [28672,4096] x 2 11.3 against
+  // 12.2 us (int8 row), [24576,3072] x 2 8.4 against 9.2 us, [14336,4096] x 2
+  // 7.5 against 7.9 us; from 5 pieces up 2 per CU stayed level or faster
+  // ([28672,8192] x 2: 20.4 against 21.0 us).
+  const int gate_per_cu = pl.np <= 4 ? 3 : 2;
+  const int per_cu = bt == 512 ? (gate || xt_rms(xt) ? 1 : 2) : (gate ? gate_per_cu : 3);
   const int64_t cap = (int64_t)num_cus * per_cu;
   // One row per team when that takes at most one more block per CU than
   // the persistent grid: otherwise a few teams per CU walk a second row

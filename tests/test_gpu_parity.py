@@ -209,7 +209,7 @@ def test_gemv_zero_k_and_empty(env):
                                    (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560),
                                    (16, 2052, 112), (33, 260, 400), (64, 2560, 6912),
                                    (32, 6912, 2560), (32, 2560, 6912), (8, 516, 20000),
-                                   (2, 100, 1008), (3, 12, 131072)])
+                                   (2, 100, 1008), (3, 12, 131072), (1, 28672, 4096)])
 def test_gate_up_relu2(env, M, N, K):
     torch, tq, oracle = env
     say(f"gate_up M={M} N={N} K={K}")
@@ -390,8 +390,9 @@ def test_quant_gemv_group(env, Ns, K, dtype):
 
 # (16400, 20480): two 256-lane teams per block walk up to 9 rows of both
 # matrices, reusing their per-row sum slots across the periodic barrier.
+# (28672, 4096): a persistent grid of 3 blocks per CU (short rows).
 @pytest.mark.parametrize("N,K", [(6912, 2560), (20, 48), (1028, 4608), (256, 28672),
-                                 (8, 40000), (16400, 20480)])
+                                 (8, 40000), (16400, 20480), (28672, 4096)])
 def test_quant_gate_up_relu2(env, N, K):
     torch, tq, oracle = env
     say(f"quant_gate_up N={N} K={K}")
