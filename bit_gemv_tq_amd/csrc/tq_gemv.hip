@@ -231,8 +231,13 @@ RegPlan plan_gemv_reg(int64_t n4, int64_t kp, int num_cus, bool gate, int xt) {
   // 12.2 us (int8 row), [24576,3072] x 2 8.4 against 9.2 us, [14336,4096] x 2
   // 7.5 against 7.9 us; from 5 pieces up 2 per CU stayed level or faster
   // ([28672,8192] x 2: 20.4 against 21.0 us).
+  // Likewise the single-matrix form takes 4 blocks per CU with short rows:
+  // [28672,4096] 7.2 against 7.5 us, [24576,3072] 5.5-5.7 against
+  // 5.8-5.9 us, [49152,2048] 7.6-7.7 against 7.8-8.2 us (level at
+  // [57344,4096] and [32768,4096]).
   const int gate_per_cu = pl.np <= 4 ? 3 : 2;
-  const int per_cu = bt == 512 ? (gate || xt_rms(xt) ? 1 : 2) : (gate ? gate_per_cu : 3);
+  const int plain_per_cu = pl.np <= 4 ? 4 : 3;
+  const int per_cu = bt == 512 ? (gate || xt_rms(xt) ? 1 : 2) : (gate ? gate_per_cu : plain_per_cu);
   const int64_t cap = (int64_t)num_cus * per_cu;
   // One row per team when that takes at most one more block per CU than
   // the persistent grid: otherwise a few teams per CU walk a second row

@@ -148,7 +148,7 @@ def test_act_quant_scale_sweep(env):
 GEMV_SHAPES = [(4, 16), (8, 32), (12, 48), (100, 1008), (36, 2064), (260, 400),
                (2560, 2560), (640, 2560), (6912, 2560), (2560, 6912),
                (4, 131072), (2052, 16), (8, 32768), (4, 32784), (28, 16384),
-               (1024, 4608), (40000, 64), (3076, 1552)]
+               (1024, 4608), (40000, 64), (3076, 1552), (28672, 4096)]
 
 
 def run_gemv(env, N, K, seed, s_w=np.float32(0.02)):
@@ -289,11 +289,12 @@ def test_gemm_small_zero_k(env):
 # teams per block walk up to 9 rows each, so their per-row sum slots are
 # reused (more than 8 rows) across the periodic barrier.  (8192, 30720): the
 # fp32 form's persistent grid is capped at the one block per CU its
-# registers allow.
+# registers allow.  (28672, 4096): a persistent grid of 4 blocks per CU
+# (short rows).
 FUSED_SHAPES = [(4, 16), (12, 48), (100, 1008), (36, 2064), (2560, 2560),
                 (6912, 2560), (2560, 6912), (8, 32768), (4, 32784), (28, 16384),
                 (28672, 8192), (8192, 28672), (8400, 20000), (14336, 4096),
-                (32776, 16400), (8192, 30720)]
+                (32776, 16400), (8192, 30720), (28672, 4096)]
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)
