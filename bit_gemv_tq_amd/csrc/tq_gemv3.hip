@@ -180,15 +180,21 @@ __global__ __launch_bounds__(reg_block_threads(LPR)) void gemv3_kernel(Gemv3Args
 struct Plan3 {
   int lpr, np, blocks;
   bool exact;
+  bool persistent;  // 256-thread blocks capped per CU, rows walked
+  int cus;
 };
 
 // As the two-bit kernel's plan: the narrowest team with at most 8 pieces per
-// lane, 64-lane teams when rows are few; grids of at most 3 blocks per CU,
-// 4 for 512-thread blocks.  At 5-8 pieces per lane a CU holds only 2 of the
-// 512-thread blocks (86-114 VGPRs), so a grid of one row per team beyond
-// that runs as a second wave of blocks; measured on MI355X it still beat a
-// grid of 2 blocks per CU whose teams walk two rows (15.9 against 16.8 us
-// at [8192,28672]: 820 blocks of one row per team).
+// lane, 64-lane teams when rows are few; grids of at most 5 blocks per CU
+// for 256-thread blocks, lowered at launch to what the compiled kernel lets
+// a CU hold (this VALU-heavy decode gains from more waves per SIMD:
+// measured on MI355X, [28672,8192] 14.0 against 14.6 us with 3 per CU,
+// [57344,4096] 14.4 against 15.2 us), and 4 for 512-thread blocks.  At
+// 5-8 pieces per lane a CU holds only 2 of the 512-thread blocks (86-114
+// VGPRs), so a grid of one row per team beyond that runs as a second wave
+// of blocks; measured on MI355X it still beat a grid of 2 blocks per CU
+// whose teams walk two rows (15.9 against 16.8 us at [8192,28672]: 820
+// blocks of one row per team), so those grids are not lowered.
 Plan3 plan3(int64_t n5, int64_t kp, int num_cus) {
   Plan3 pl{};
   int lpr = 16;
@@ -201,17 +207,31 @@ Plan3 plan3(int64_t n5, int64_t kp, int num_cus) {
   const int bt = reg_block_threads(lpr);
   const int64_t teams = bt / lpr;
   int64_t blocks = (n5 + teams - 1) / teams;
-  const int64_t cap = (int64_t)num_cus * (bt == 512 ? 4 : 3);
+  const int64_t cap = (int64_t)num_cus * (bt == 512 ? 4 : 5);
+  pl.persistent = blocks > cap && bt != 512;
   if (blocks > cap) blocks = cap;
   pl.blocks = (int)(blocks < 1 ? 1 : blocks);
+  pl.cus = num_cus;
   return pl;
+}
+
+template <int LPR, int NP, bool EXACT>
+tq_status launch3_form(const Plan3 &pl, const Gemv3Args &a, hipStream_t s) {
+  auto kernel = gemv3_kernel<LPR, NP, EXACT>;
+  const dim3 block(reg_block_threads(LPR));
+  int blocks = pl.blocks;
+  if (pl.persistent) {
+    static std::atomic<int> occ;
+    const int n = resident_blocks(kernel, (int)block.x, occ);
+    if (n > 0 && (int64_t)blocks > (int64_t)n * pl.cus) blocks = n * pl.cus;
+  }
+  return launch(kernel, dim3(blocks), block, 0, s, a);
 }
 
 template <int LPR, int NP>
 tq_status launch3_np(const Plan3 &pl, const Gemv3Args &a, hipStream_t s) {
-  const dim3 grid(pl.blocks), block(reg_block_threads(LPR));
-  return pl.exact ? launch(gemv3_kernel<LPR, NP, true>, grid, block, 0, s, a)
-                  : launch(gemv3_kernel<LPR, NP, false>, grid, block, 0, s, a);
+  return pl.exact ? launch3_form<LPR, NP, true>(pl, a, s)
+                  : launch3_form<LPR, NP, false>(pl, a, s);
 }
 
 template <int LPR>

@@ -519,15 +519,7 @@ tq_status launch_resident(K kernel, std::atomic<int> &occ, const RegPlan &pl, di
   int blocks = pl.blocks;
   RegArgs a = args;
   if (pl.persistent) {
-    int n = occ.load(std::memory_order_relaxed);
-    if (n == 0) {
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, (int)block.x, 0) !=
-              hipSuccess || n < 1) {
-        (void)hipGetLastError();
-        n = -1;  // unknown: keep the plan
-      }
-      occ.store(n, std::memory_order_relaxed);
-    }
+    const int n = resident_blocks(kernel, (int)block.x, occ);  // -1: keep the plan
     if (n > 0 && (int64_t)blocks > (int64_t)n * pl.cus) {
       blocks = n * pl.cus;
       a.round_cus = 0;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/tq.h"
 
 namespace tq {
@@ -50,6 +52,24 @@ tq_status launch(void (*kernel)(Params...), dim3 grid, dim3 block,
     return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
   };
   return call(static_cast<Params>(args)...);
+}
+
+// Blocks of `kernel` (launched with `threads` threads, no dynamic LDS) that
+// one CU holds, asked of the runtime once and kept in `cache` (0: not asked
+// yet, -1: unknown).  Persistent grids are capped at this times the CU
+// count, so that no block of them waits for a second wave.
+template <typename K>
+int resident_blocks(K kernel, int threads, std::atomic<int> &cache) {
+  int n = cache.load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess ||
+        n < 1) {
+      (void)hipGetLastError();
+      n = -1;
+    }
+    cache.store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 // RMSNorm-folded quantization of M rows (tq_act_quant.hip), used by the
