@@ -286,7 +286,7 @@ struct QuadPlan {
 // to 8 (the compiler's gfx950 register counts of every RG x NQ x form; 0:
 // no NQ fits; the gated form's epilogue alone needs more than 128).
 constexpr int quad_max_nq(int nm, int rg, int maxw) {
-  if (maxw > 8) return nm == 1 ? (rg == 1 ? 3 : rg == 2 ? 2 : rg == 4 ? 1 : 0) : 0;
+  if (maxw > 8) return nm == 1 ? (rg == 1 ? 3 : rg == 2 ? 2 : rg <= 4 ? 1 : 0) : 0;
   return nm == 1 ? (rg <= 4 ? 4 : 3) : (rg <= 2 ? 4 : 3);
 }
 
@@ -295,19 +295,30 @@ constexpr int quad_lds(int rg, int nq, int nm, int w) {
          (nm * rg * 4 * kSlotPad * quad_wave_stride(w) + (w > 8 ? 16 : 8)) * 16;
 }
 
-// Quads per block: the largest RG that still gives about 5/8 of a block per
-// CU (measured on MI355X: a larger RG re-reads less of the activation tile,
-// too few blocks leave CUs idle).  Then one group per wave and pass, with
-// as many waves as the register table above and the LDS allow.
+// Quads per block: the RG (of those instantiated) that moves the fewest
+// bytes through the busiest CU, i.e. blocks per CU (rounded up) times the
+// K x (4 RG nm + 16) bytes of weights and activation tile one block reads
+// (operand arrival, set by how fast a CU's L1 fills, dominates a pass).
+// Ties go to the larger RG.  This keeps the earlier plans (RG = 2 / 4 / 8 at
+// M <= 16 / 32 / 64 for [6912,2560], RG = 1 / 2 at M <= 16 / 32 for
+// [2560,6912]) and takes RG = 3 at M = 64 for [2560,6912] (216 blocks of
+// 193 KB instead of 160 of 221 KB; measured on MI355X 7.6 against 8.1 us,
+// the gated pair 9.6 against 10.6 us).  Then one group per wave and pass,
+// with as many waves as the register table above and the LDS allow.
+constexpr int kQuadRgs[] = {8, 4, 3, 2, 1};
+
 QuadPlan plan_quad(int64_t M, int64_t n4, int64_t K, bool gate, int num_cus, int &mtiles) {
   const int nm = gate ? 2 : 1;
   mtiles = (int)((M + 15) / 16);
   QuadPlan pl{1, 1, 1};
-  for (int rg : {8, 4, 2}) {
+  int64_t best = -1;
+  for (int rg : kQuadRgs) {
     if (rg * nm > 8) continue;
-    if ((n4 + 4 * rg - 1) / (4 * rg) * mtiles >= (5 * num_cus) / 8) {
+    const int64_t blocks = (n4 + 4 * rg - 1) / (4 * rg) * mtiles;
+    const int64_t cost = (blocks + num_cus - 1) / num_cus * (4 * rg * nm + 16);
+    if (best < 0 || cost < best) {
+      best = cost;
       pl.rg = rg;
-      break;
     }
   }
   auto fits = [&](int nq, int w) {
@@ -364,6 +375,7 @@ tq_status launch_gemm(GemmArgs a, int num_cus, hipStream_t s) {
   switch (pl.rg) {
     case 1: return launch_quad_nq<1, kGate>(pl, a, grid, s);
     case 2: return launch_quad_nq<2, kGate>(pl, a, grid, s);
+    case 3: return launch_quad_nq<3, kGate>(pl, a, grid, s);
     case 4: return launch_quad_nq<4, kGate>(pl, a, grid, s);
     case 8:
       if constexpr (!kGate) return launch_quad_nq<8, kGate>(pl, a, grid, s);

@@ -236,7 +236,8 @@ def test_gate_up_relu2(env, M, N, K):
 # ------------------------------------------------------------------ gemm small
 # M = 2 runs on the vector ALU (K <= 16384), M >= 3 on the matrix cores.
 # The matrix-core plans these shapes take (quads per block RG, one 256-byte
-# group per wave and pass, waves W, passes over K): every RG in {1, 2, 4, 8},
+# group per wave and pass, waves W, passes over K): every RG in
+# {1, 2, 3, 4, 8} (3 at M = 64, N = 2560, with K a multiple of 256 and not),
 # W 1..16, blocks of up to 8 and up to 16 waves, one to 32 passes, ragged K
 # (not a multiple of 256) and ragged N (not a multiple of 16 RG).
 GEMM_CASES = [(m, 6912, 2560) for m in (2, 3, 4, 8, 16, 32, 64)] + \
@@ -245,7 +246,7 @@ GEMM_CASES = [(m, 6912, 2560) for m in (2, 3, 4, 8, 16, 32, 64)] + \
               (63, 64, 16), (48, 2052, 112),
               (2, 20, 16), (3, 52, 4112), (4, 100, 16384), (4, 64, 16400),
               (2, 36, 1040), (4, 8, 32768), (16, 512, 28672), (2, 12, 20000),
-              (2, 36, 12288), (3, 8, 131072)]
+              (2, 36, 12288), (3, 8, 131072), (64, 2560, 6928)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
