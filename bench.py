@@ -18,10 +18,11 @@ Timing:
     i mod C of every pool (C = the pool's copy count).
   * Steps and kernel loops are captured in HIP graphs; a spin kernel queued
     before the start event keeps the host ahead, so HIP events on the
-    launch stream measure GPU execution only.  A step graph holds 12
-    consecutive steps (graph g: steps 12g .. 12g + 11), so the fixed cost of
-    a graph replay (about 5 us) is spread as in a decode graph of a layer
-    stack; the time with one step per graph is reported too.
+    launch stream measure GPU execution only.  The K timed steps are
+    captured as ceil(K / 12) graphs of consecutive steps whose sizes differ
+    by at most one (K = 20: two graphs of 10), so the fixed cost of a graph
+    replay (about 5 us) is spread as in a decode graph of a layer stack;
+    the time with one step per graph is reported too.
   * roofline: the dominant kernel (the fused [8192, 28672] launch) is timed
     as graphs of 96 back-to-back launches over its pool; algorithmic bytes
     per launch (packed weights + bf16 x + int8 x written + fp32 scale +
@@ -97,6 +98,16 @@ def algo_bytes(N, K, M=1):
 def algo_bytes_fused(N, K):
     # packed weights + bf16 row read + int8 row and scale written + fp32 y
     return N * K // 4 + 2 * K + K + 4 + 4 * N
+
+
+def graph_sizes(steps):
+    """Steps per graph for `steps` consecutive timed steps: ceil(steps /
+    STEP_COPIES) graphs whose sizes differ by at most one, so no step is
+    charged a graph of its own (a graph replay has a fixed cost of about
+    5 us on this part, which a graph of one 3-kernel step would charge to
+    every step, while a decode graph holds a whole layer stack)."""
+    n = -(-steps // STEP_COPIES)
+    return [steps // n + (1 if g < steps % n else 0) for g in range(n)]
 
 
 def code_only(text):
@@ -452,23 +463,21 @@ def main():
         return run
 
     def step_graphs(fn, steps):
-        """Graphs for steps 0 .. steps-1: STEP_COPIES consecutive steps per
-        graph (3 kernel nodes each, as a decode graph holds a whole layer
-        stack: a graph replay has a fixed cost of about 5 us on this part,
-        which a graph of one 3-kernel step would charge to every step), the
-        remainder as one-step graphs."""
-        S = STEP_COPIES
-        full = [timer.graph(steps_of(fn, g * S, S)) for g in range(steps // S)]
-        rest = [timer.graph(steps_of(fn, (steps // S) * S + j, 1)) for j in range(steps % S)]
-        return full + rest
+        """Graphs for steps 0 .. steps-1, consecutive steps per graph as
+        graph_sizes gives them, each with its size."""
+        out, i0 = [], 0
+        for n in graph_sizes(steps):
+            out.append((timer.graph(steps_of(fn, i0, n)), n))
+            i0 += n
+        return out
 
     def warm(graphs, warmup):
         done = 0
-        for g in graphs:
+        for g, n in graphs:
             if done >= warmup:
                 break
             g.replay()
-            done += STEP_COPIES
+            done += n
         torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- step
@@ -476,7 +485,7 @@ def main():
     graphs = step_graphs(step, args.steps)
     warm(graphs, args.warmup)
     wall0 = time.perf_counter()
-    ms_step = timer.time_sequence(graphs, args.steps)
+    ms_step = timer.time_sequence([g for g, _ in graphs], args.steps)
     wall = time.perf_counter() - wall0
     step_wbytes = sum(weight_bytes(*s) for s in SHAPES.values())
     value = step_wbytes / (ms_step * 1e-3) / 1e9
@@ -488,7 +497,7 @@ def main():
     del singles
     graphs_u = step_graphs(step_unfused, args.steps)
     warm(graphs_u, STEP_COPIES)
-    ms_step_u = timer.time_sequence(graphs_u, args.steps)
+    ms_step_u = timer.time_sequence([g for g, _ in graphs_u], args.steps)
     log(f"unfused step (act_quant + gemv launches): {ms_step_u * 1e3:.2f} us")
     del graphs_u
 
@@ -613,7 +622,7 @@ def main():
             "pool_bytes_min": POOL_BYTES_MIN,
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-            "steps_per_graph": STEP_COPIES,
+            "steps_per_graph": graph_sizes(args.steps),
             "ms_per_step_one_step_per_graph": round(ms_step_1, 5),
             "unfused_ms_per_step": round(ms_step_u, 5),
             "read_ceiling": ceiling,

@@ -34,6 +34,19 @@ def test_byte_counts():
     assert step == 121_864_192
 
 
+def test_graph_sizes_cover_every_step_evenly():
+    # every timed step is in a multi-step graph of at most 12 steps; sizes
+    # differ by at most one (no one-step remainder graphs)
+    assert bench.graph_sizes(20) == [10, 10]
+    assert bench.graph_sizes(12) == [12]
+    assert bench.graph_sizes(5) == [5]
+    assert bench.graph_sizes(1) == [1]
+    for k in (13, 50, 199, 200, 1000):
+        g = bench.graph_sizes(k)
+        assert sum(g) == k and max(g) <= bench.STEP_COPIES
+        assert max(g) - min(g) <= 1 and len(g) == -(-k // bench.STEP_COPIES)
+
+
 def test_code_only_ignores_comments_and_blank_lines():
     a = "int x = 1;  // one\n\n// a comment line\nint y = 2;\n"
     b = "int x = 1;\nint y = 2;   // two\n\n\n"
