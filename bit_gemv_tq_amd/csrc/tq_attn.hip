@@ -60,7 +60,6 @@ struct AttnShape {
   static constexpr int CH = TPB * kT;         // tokens per block step
   static constexpr int NV = kT * G;           // partial dots per lane
   static constexpr int VPL = NV / LPT;        // complete sums per lane
-  static constexpr bool kPrefetchV = kT <= 8;  // V rows loaded with K rows
   static_assert(NV % LPT == 0 && VPL >= 1, "butterfly shape");
   static_assert(CH >= kAttnMinChunk, "workspace sized for 64-token steps");
 };
