@@ -37,7 +37,8 @@ Timing:
     same pool) and each form's fraction of it.
   * rows: every hot-path row timed the same way -- act_quant, gemv, fused
     gate/up + relu^2 (2B-4T and 70B-class), the decode chain (30 2B-4T
-    layers, 8 70B-class layers), the small-batch MFMA GEMM
+    layers, graph-captured and, for comparison, launched eagerly; 8
+    70B-class layers), the small-batch MFMA GEMM
     (M = 4, 16, 64), the absmean
     ternarizer, split-KV decode attention and the 30-layer decode-step chain
     (graph-captured).
@@ -224,7 +225,9 @@ def cpu_baseline(budget_s=10.0, max_threads=16):
                 for a, b in zip(cuts, cuts[1:]) if b > a]
         return [j.result() for j in jobs]
 
-    def run(nt):
+    step_bytes = sum(weight_bytes(*s) for s in SHAPES.values())
+
+    def run(nt, budget):
         reps, t0 = 0, time.perf_counter()
         while True:
             for name, (N, K) in SHAPES.items():
@@ -235,19 +238,24 @@ def cpu_baseline(budget_s=10.0, max_threads=16):
                     gemv_split(name, N, q, s, nt)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 400:
+            if el >= budget or reps >= 80:
                 return reps, el
 
-    step_bytes = sum(weight_bytes(*s) for s in SHAPES.values())
-    r1, e1 = run(1)
-    rn, en = run(threads)
+    def median_of(nt, runs=5):
+        """Median weight GB/s of `runs` timed runs (the budget split
+        between them), with the runs themselves."""
+        rs = [run(nt, budget_s / runs) for _ in range(runs)]
+        rates = sorted(step_bytes * r / e / 1e9 for r, e in rs)
+        return rates[len(rates) // 2], rs
+
+    one, rs1 = median_of(1)
+    alln, rsn = median_of(threads)
     pool.shutdown()
-    one = step_bytes * r1 / e1 / 1e9
-    alln = step_bytes * rn / en / 1e9
+    fmt = lambda rs: ", ".join(f"{r} in {e:.2f} s" for r, e in rs)
     return {"value": round(alln, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{rn} full steps (all three shapes, act_quant + GEMV) in {en:.1f} s "
-                       f"on {threads} threads, output rows split over threads; "
-                       f"one thread: {r1} steps in {e1:.1f} s"),
+            "sample": (f"median of 5 runs of full steps (all three shapes, act_quant + "
+                       f"GEMV) on {threads} threads, output rows split over threads "
+                       f"({fmt(rsn)}); one thread: median of 5 ({fmt(rs1)})"),
             "one_thread_value": round(one, 4),
             "host": {"cpu_model": model, "nproc": ncpu, "usable_cores": usable}}
 
@@ -1031,6 +1039,28 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
             "launches_per_token": launches * workloads.CHAIN_LAYERS}
         log(f"{key}: {rows[key]}")
         del g, chain
+    # the same fused chain launched eagerly (no graph): every launch goes
+    # through the Python binding, so this is the host's launch rate, not the
+    # GPU's -- what graph capture removes
+    chain = DecodeChain(layers, dev, fused=True)
+    chain.step(h0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n_eager = 10
+    e0.record()
+    for _ in range(n_eager):
+        chain.step(h0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_eager
+    rows["decode_chain_30x2b4t_eager"] = {
+        "us_per_token": round(ms * 1e3, 2),
+        "tokens_per_s": round(1e3 / ms, 1),
+        "launches_per_token": 4 * workloads.CHAIN_LAYERS,
+        "note": "fused chain launched from Python without a graph (host-bound)"}
+    log(f"decode_chain_30x2b4t_eager: {rows['decode_chain_30x2b4t_eager']}")
+    del chain
     del layers
 
     # a6 at the 70B-class shapes: 8 layers (grouped q/k/v [8192,1024,1024],
