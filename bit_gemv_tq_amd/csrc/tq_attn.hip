@@ -13,9 +13,10 @@
 // atomics), so identical calls give identical bits.  The op streams the KV
 // cache once: HBM bound at long contexts.
 //
-// Chunk pass: block (g, c) handles the G query heads of KV head g over the
-// tokens of chunk c (at most kAttnMaxSplits chunks per KV head), in steps of
-// STEP tokens.  A token row of one KV head (D bf16 = 2D bytes) is read by
+// Chunk pass: block (g, c) of 4 or 8 waves handles the G query heads of KV
+// head g over the tokens of chunk c (at most kAttnMaxSplits chunks per KV
+// head, fewer where that keeps every CU to one block; plan in
+// launch_attn_g), in steps of STEP tokens.  A token row of one KV head (D bf16 = 2D bytes) is read by
 // LPT = D/8 consecutive lanes, 16 bytes each; a lane slot takes kT tokens per
 // step, and the next step's rows are loaded during this step's arithmetic.  The kT*G partial dots of a
 // slot are summed by a reduce-scatter butterfly over its LPT lanes.  Scores,
@@ -51,11 +52,11 @@ constexpr int kCombineBatch =  // rows per thread
 // Per (G, D, kT): lanes per token row, token slots, tokens per block step.
 // kT (tokens per lane slot and step) is at least LPT/G so that every lane
 // ends the butterfly with a complete sum.
-template <int G, int D, int KT>
+template <int G, int D, int KT, int NW>
 struct AttnShape {
   static constexpr int LPT = D / 8;          // lanes per token row
   static constexpr int TPW = kWave / LPT;    // token slots per wave
-  static constexpr int TPB = kAttnNW * TPW;  // token slots per block
+  static constexpr int TPB = NW * TPW;       // token slots per block
   static constexpr int kT = KT;
   static constexpr int CH = TPB * kT;         // tokens per block step
   static constexpr int NV = kT * G;           // partial dots per lane
@@ -196,11 +197,11 @@ __device__ __forceinline__ float add_lane_xor(float v) {
   }
 }
 
-template <int G, int D, int KT>
-__global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
-  using Sh = AttnShape<G, D, KT>;
+template <int G, int D, int KT, int NW>
+__global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
+  using Sh = AttnShape<G, D, KT, NW>;
   constexpr int LPT = Sh::LPT, TPW = Sh::TPW, kT = Sh::kT, STEP = Sh::CH;
-  constexpr int NV = Sh::NV, VPL = Sh::VPL, NW = kAttnNW;
+  constexpr int NV = Sh::NV, VPL = Sh::VPL, NT = NW * kWave;
   // Dynamic LDS: scores [G][chunk], then weights; after the P.V loop the
   // per-wave outputs [NW][G][D].
   extern __shared__ float s_lds[];
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
     float m[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) m[j] = -INFINITY;
-    for (int i = threadIdx.x; i < n; i += kAttnThreads)
+    for (int i = threadIdx.x; i < n; i += NT)
 #pragma unroll
       for (int j = 0; j < G; ++j) m[j] = fmaxf(m[j], s_lds[j * chunk + i]);
 #pragma unroll
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
     float sacc[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) sacc[j] = 0.0f;
-    for (int i = threadIdx.x; i < n; i += kAttnThreads)
+    for (int i = threadIdx.x; i < n; i += NT)
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const float p = expf(s_lds[j * chunk + i] - mx[j]);
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(AttnArgs a) {
   // 5. this chunk's result: the output itself when it is the only chunk,
   // else a partial row
   constexpr int RS = D + 4;  // partial row stride (floats)
-  for (int idx = threadIdx.x; idx < G * D; idx += kAttnThreads) {
+  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
     const int j = idx / D, d = idx % D;
     float o = o_red[j * D + d];
 #pragma unroll
@@ -465,13 +466,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(
   }
 }
 
-template <int G, int D, int KT>
+// One pass of NW-wave blocks, chunks of whole steps, at most `smax` chunks
+// per KV head.
+template <int G, int D, int KT, int NW>
 tq_status launch_attn(const float *q, const void *k, const void *v, int H,
                       int Hkv, int L, float scale, float *out, float *part,
-                      hipStream_t s) {
-  // At most kAttnMaxSplits chunks per KV head, each a whole number of steps.
-  constexpr int STEP = AttnShape<G, D, KT>::CH;
-  const int steps = (L + STEP * kAttnMaxSplits - 1) / (STEP * kAttnMaxSplits);
+                      int smax, hipStream_t s) {
+  constexpr int STEP = AttnShape<G, D, KT, NW>::CH;
+  const int steps = (L + STEP * smax - 1) / (STEP * smax);
   AttnArgs a;
   a.q = q;
   a.k = static_cast<const uint16_t *>(k);
@@ -483,39 +485,67 @@ tq_status launch_attn(const float *q, const void *k, const void *v, int H,
   a.scale = scale;
   a.part = part;
   a.out = out;
-  constexpr int kOutFloats = kAttnNW * G * D;
+  constexpr int kOutFloats = NW * G * D;
   const size_t lds = (size_t)(G * a.chunk > kOutFloats ? G * a.chunk : kOutFloats) * 4;
-  if (tq_status st = allow_dynamic_lds((const void *)attn_chunk_kernel<G, D, KT>, (int)lds))
+  if (tq_status st = allow_dynamic_lds((const void *)attn_chunk_kernel<G, D, KT, NW>, (int)lds))
     return st;
-  if (tq_status st = launch(attn_chunk_kernel<G, D, KT>, dim3(Hkv, a.S),
-                            dim3(kAttnThreads), lds, s, a))
+  if (tq_status st = launch(attn_chunk_kernel<G, D, KT, NW>, dim3(Hkv, a.S),
+                            dim3(NW * kWave), lds, s, a))
     return st;
   if (a.S == 1) return TQ_OK;
   return launch(attn_combine_kernel, dim3(H, D / kCombineDims), dim3(kAttnThreads), 0, s,
                 static_cast<const float *>(part), a.S, D, out);
 }
 
-// Chunk size by context length: short contexts take the small chunks.
+// Launch plan by context length (measured on MI355X, 20 query / 5 KV heads,
+// D = 128, graphs of 16 calls over >= 1 GiB of KV copies):
+//  * short contexts whose 4-wave chunk blocks (64-token steps, up to 64
+//    chunks per KV head) number at most one per CU keep that plan
+//    (L = 2048: 10.3 us against 10.7 with the plan below);
+//  * otherwise 8-wave blocks (steps twice as long, so half as many per
+//    wave) with at most CUs / Hkv chunks per KV head, so no CU holds two
+//    blocks: L = 4096 / 8192 11.8-12.0 / 14.1 us against 13.5 / 15.7 us,
+//    L = 12288 / 32768 / 131072 15.2 / 25.4-25.6 / 72.2-72.8 us against
+//    16.3-16.4 / 28.8-29.6 / 80.0-81.2 us for 4-wave blocks with up to 64
+//    chunks (both capped: 4-wave blocks 28.0 us at 32768; uncapped 8-wave
+//    blocks 33.3 us).
 constexpr int kAttnShortL = 8192;
+constexpr int kAttnWideNW = 8;
+constexpr int kAttnScoreLds = 128 * 1024;  // bytes of scores per chunk block
 
 template <int G, int D>
 tq_status launch_attn_g(const float *q, const void *k, const void *v, int H,
                         int Hkv, int L, float scale, float *out, float *part,
-                        hipStream_t s) {
+                        int num_cus, hipStream_t s) {
+  constexpr int KS = kt_short<G, D>(), KL = kt_long<G, D>();
+  if (L <= kAttnShortL) {
+    constexpr int STEP = AttnShape<G, D, KS, kAttnNW>::CH;
+    const int steps = (L + STEP * kAttnMaxSplits - 1) / (STEP * kAttnMaxSplits);
+    const int chunks = (L + steps * STEP - 1) / (steps * STEP);
+    if ((int64_t)Hkv * chunks <= num_cus)
+      return launch_attn<G, D, KS, kAttnNW>(q, k, v, H, Hkv, L, scale, out, part,
+                                            kAttnMaxSplits, s);
+  }
+  // At most one block per CU, but chunks short enough that the G score rows
+  // of a chunk stay within kAttnScoreLds of LDS (G * chunk fp32).
+  int cap = num_cus / Hkv;
+  const int lds_min = (int)(((int64_t)L * G * 4 + kAttnScoreLds - 1) / kAttnScoreLds);
+  cap = cap < lds_min ? lds_min : cap;
+  cap = cap < 1 ? 1 : (cap > kAttnMaxSplits ? kAttnMaxSplits : cap);
   if (L <= kAttnShortL)
-    return launch_attn<G, D, kt_short<G, D>()>(q, k, v, H, Hkv, L, scale, out, part, s);
-  return launch_attn<G, D, kt_long<G, D>()>(q, k, v, H, Hkv, L, scale, out, part, s);
+    return launch_attn<G, D, KS, kAttnWideNW>(q, k, v, H, Hkv, L, scale, out, part, cap, s);
+  return launch_attn<G, D, KL, kAttnWideNW>(q, k, v, H, Hkv, L, scale, out, part, cap, s);
 }
 
 template <int D>
 tq_status launch_attn_d(int G, const float *q, const void *k, const void *v,
                         int H, int Hkv, int L, float scale, float *out,
-                        float *part, hipStream_t s) {
+                        float *part, int num_cus, hipStream_t s) {
   switch (G) {
-    case 1: return launch_attn_g<1, D>(q, k, v, H, Hkv, L, scale, out, part, s);
-    case 2: return launch_attn_g<2, D>(q, k, v, H, Hkv, L, scale, out, part, s);
-    case 4: return launch_attn_g<4, D>(q, k, v, H, Hkv, L, scale, out, part, s);
-    case 8: return launch_attn_g<8, D>(q, k, v, H, Hkv, L, scale, out, part, s);
+    case 1: return launch_attn_g<1, D>(q, k, v, H, Hkv, L, scale, out, part, num_cus, s);
+    case 2: return launch_attn_g<2, D>(q, k, v, H, Hkv, L, scale, out, part, num_cus, s);
+    case 4: return launch_attn_g<4, D>(q, k, v, H, Hkv, L, scale, out, part, num_cus, s);
+    case 8: return launch_attn_g<8, D>(q, k, v, H, Hkv, L, scale, out, part, num_cus, s);
   }
   return TQ_ERR_SHAPE;
 }
@@ -543,9 +573,9 @@ extern "C" tq_status tq_attn_decode(const float *q, const void *k_cache,
   if (tq_status s = current_device(&dev)) return s;
   auto *part = static_cast<float *>(workspace);
   return D == 128 ? launch_attn_d<128>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
-                                       (int)L, scale, out, part, stream)
+                                       (int)L, scale, out, part, dev.num_cus, stream)
                   : launch_attn_d<64>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
-                                      (int)L, scale, out, part, stream);
+                                      (int)L, scale, out, part, dev.num_cus, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -613,7 +643,7 @@ extern "C" tq_status tq_attn_decode_noalloc(const float *q, const void *k_cache,
   if (tq_status s = scratch_address(dev.device, &part)) return s;
   // At most kAttnMaxSplits chunks of H rows of D + 4 floats are written.
   return D == 128 ? launch_attn_d<128>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
-                                       (int)L, scale, out, part, stream)
+                                       (int)L, scale, out, part, dev.num_cus, stream)
                   : launch_attn_d<64>((int)G, q, k_cache, v_cache, (int)H, (int)Hkv,
-                                      (int)L, scale, out, part, stream);
+                                      (int)L, scale, out, part, dev.num_cus, stream);
 }

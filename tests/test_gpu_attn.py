@@ -5,9 +5,11 @@ softmax, exact cases (one token: out == v; identical keys), and bitwise
 determinism across calls.
 
 Covered: one chunk (the chunk pass writes the output), the combine over 2
-to 64 chunks of one or several steps, both step sizes (contexts up to 8192
-take the smaller), ragged last steps and chunks, and one workspace reused
-across calls of different lengths.
+to 64 chunks of one or several steps, both block sizes (4 waves for short
+contexts whose chunks fit one block per CU, else 8 waves with the chunk
+count capped at CUs / KV heads), both step sizes (contexts up to 8192 take
+the smaller), ragged last steps and chunks, and one workspace reused across
+calls of different lengths.
 
 Tolerance (derived from the kernel's fp32 arithmetic, per head h):
   E   = gamma(13) * scale * max_t sum_d |q[h,d] k[t,d]|   (score error: an
@@ -54,26 +56,43 @@ def gamma(n):
     return n * U / (1 - n * U)
 
 
-def chunk_shape(G, D, L):
-    """Tokens per lane slot over a chunk, and tokens per chunk, of the
-    kernel's layout: per step at most 8 per slot (4 up to L = 8192), at
-    least D/8/G; whole steps per chunk, at most 64 chunks."""
+def num_cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def chunk_shape(G, D, L, Hkv, cus):
+    """Tokens per lane slot over a chunk, tokens per chunk and waves per
+    block of the kernel's plan: 4-wave blocks (steps of at most 4 tokens per
+    slot, at least D/8/G; up to 64 chunks per KV head) for contexts up to
+    8192 whose chunks number at most one block per CU; otherwise 8-wave
+    blocks (at most 4 tokens per slot up to 8192, 8 beyond; at least D/8/G)
+    with at most CUs / Hkv chunks per KV head (more where a chunk's G score
+    rows would pass 128 KiB of LDS).  Whole steps per chunk."""
     lpt = D // 8                                   # lanes per token row
-    tpb = 4 * (64 // lpt)                          # token slots per block
-    kt = max(lpt // G, min(32 // G, 8))
+    tpw = 64 // lpt                                # token slots per wave
+    kt_long = max(lpt // G, min(32 // G, 8))
+    kt_short = max(lpt // G, min(kt_long, 4))
     if L <= 8192:
-        kt = max(lpt // G, min(kt, 4))
-    steps = -(-L // (tpb * kt * 64))
-    return steps * kt, steps * tpb * kt
+        step = 4 * tpw * kt_short
+        steps = -(-L // (step * 64))
+        if Hkv * -(-L // (steps * step)) <= cus:
+            return steps * kt_short, steps * step, 4
+    kt = kt_short if L <= 8192 else kt_long
+    lds_min = -(-L * G * 4 // (128 * 1024))        # scores of a chunk <= 128 KiB
+    cap = min(64, max(1, cus // Hkv, lds_min))
+    step = 8 * tpw * kt
+    steps = -(-L // (step * cap))
+    return steps * kt, steps * step, 8
 
 
 def bound(q, k, v, ref, scale, L, G, D):
     """Per-element error bound of the kernel's fp32 arithmetic (see above)."""
     kf = (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     vf = (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    kt, chunk = chunk_shape(G, D, L)
-    dN = kt + 8        # a slot's tokens, 3 shuffle levels, 4 waves
-    dD = -(-chunk // 256) + 11
+    kt, chunk, nw = chunk_shape(G, D, L, q.shape[0] // G, num_cus())
+    dN = kt + 4 + nw   # a slot's tokens, 3 shuffle levels, the waves
+    dD = -(-chunk // (64 * nw)) + 7 + nw
     H = q.shape[0]
     out = np.empty_like(ref)
     for h in range(H):
@@ -105,10 +124,12 @@ def check(env, L, H=20, Hkv=5, D=128, seed=0, kscale=1.0, data=None, ws=None):
     return qt, kt, vt, out
 
 
-# here 64-token steps up to L = 8192 (one chunk up to 64 tokens, 64 chunks of
-# 2 steps at 8192), 128-token steps beyond (131072: 64 chunks of 16 steps)
-@pytest.mark.parametrize("L", [1, 7, 16, 64, 65, 100, 2048, 2049, 8192, 8193,
-                               32768, 131072])
+# here (256 CUs, 5 KV heads): 4-wave blocks of 64-token steps up to L = 3264
+# (one chunk up to 64 tokens, 48 chunks at 3072), then 8-wave blocks of
+# 128-token steps up to 8192 and 256-token steps beyond, at most 51 chunks
+# per KV head (131072: 32 chunks of 16 steps)
+@pytest.mark.parametrize("L", [1, 7, 16, 64, 65, 100, 2048, 2049, 3264, 3265, 4096,
+                               8192, 8193, 32768, 131072])
 def test_attn_2b4t_heads(env, L):
     check(env, L, seed=L)
 
@@ -118,6 +139,14 @@ def test_attn_2b4t_heads(env, L):
                                      (64, 8, 128), (16, 2, 64)])
 def test_attn_group_sizes(env, H, Hkv, D, L):
     check(env, L, H, Hkv, D, seed=H + D + L)
+
+
+@pytest.mark.parametrize("H,Hkv,D,L", [(256, 32, 64, 40000), (64, 8, 128, 131072)])
+def test_attn_many_kv_heads_long(env, H, Hkv, D, L):
+    # many KV heads at long contexts: few chunks per KV head, so the chunk
+    # length is bounded by the LDS that holds its scores (256 / 32 heads:
+    # 10 chunks of 4096 tokens rather than 8 of 5120)
+    check(env, L, H, Hkv, D, seed=H + L)
 
 
 def test_attn_workspace_reuse(env):
