@@ -287,7 +287,7 @@ struct QuadPlan {
 // no NQ fits; the gated form's epilogue alone needs more than 128).
 constexpr int quad_max_nq(int nm, int rg, int maxw) {
   if (maxw > 8) return nm == 1 ? (rg == 1 ? 3 : rg == 2 ? 2 : rg <= 4 ? 1 : 0) : 0;
-  return nm == 1 ? (rg <= 4 ? 4 : 3) : (rg <= 2 ? 4 : 3);
+  return nm == 1 ? (rg <= 4 ? 4 : 3) : (rg <= 2 ? 4 : rg <= 4 ? 3 : 1);
 }
 
 constexpr int quad_lds(int rg, int nq, int nm, int w) {
@@ -303,8 +303,11 @@ constexpr int quad_lds(int rg, int nq, int nm, int w) {
 // M <= 16 / 32 / 64 for [6912,2560], RG = 1 / 2 at M <= 16 / 32 for
 // [2560,6912]) and takes RG = 3 at M = 64 for [2560,6912] (216 blocks of
 // 193 KB instead of 160 of 221 KB; measured on MI355X 7.6 against 8.1 us,
-// the gated pair 9.6 against 10.6 us).  Then one group per wave and pass,
-// with as many waves as the register table above and the LDS allow.
+// the gated pair 9.6 against 10.6 us) and, for the gated pair, RG = 8 at
+// M = 48 and 64 for [6912,2560] (one block per CU instead of two on most:
+// 10.1 / 10.3 against 11.0 / 11.9-12.6 us; 231 VGPRs, no spills).  Then one
+// group per wave and pass, with as many waves as the register table above
+// and the LDS allow.
 constexpr int kQuadRgs[] = {8, 4, 3, 2, 1};
 
 QuadPlan plan_quad(int64_t M, int64_t n4, int64_t K, bool gate, int num_cus, int &mtiles) {
@@ -313,7 +316,7 @@ QuadPlan plan_quad(int64_t M, int64_t n4, int64_t K, bool gate, int num_cus, int
   QuadPlan pl{1, 1, 1};
   int64_t best = -1;
   for (int rg : kQuadRgs) {
-    if (rg * nm > 8) continue;
+    if (rg * nm > 16) continue;
     const int64_t blocks = (n4 + 4 * rg - 1) / (4 * rg) * mtiles;
     const int64_t cost = (blocks + num_cus - 1) / num_cus * (4 * rg * nm + 16);
     if (best < 0 || cost < best) {
@@ -377,9 +380,7 @@ tq_status launch_gemm(GemmArgs a, int num_cus, hipStream_t s) {
     case 2: return launch_quad_nq<2, kGate>(pl, a, grid, s);
     case 3: return launch_quad_nq<3, kGate>(pl, a, grid, s);
     case 4: return launch_quad_nq<4, kGate>(pl, a, grid, s);
-    case 8:
-      if constexpr (!kGate) return launch_quad_nq<8, kGate>(pl, a, grid, s);
-      break;
+    case 8: return launch_quad_nq<8, kGate>(pl, a, grid, s);
   }
   return TQ_ERR_LAUNCH;
 }

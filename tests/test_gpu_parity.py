@@ -209,7 +209,8 @@ def test_gemv_zero_k_and_empty(env):
                                    (4, 6912, 2560), (17, 68, 80), (64, 6912, 2560),
                                    (16, 2052, 112), (33, 260, 400), (64, 2560, 6912),
                                    (32, 6912, 2560), (32, 2560, 6912), (8, 516, 20000),
-                                   (2, 100, 1008), (3, 12, 131072), (1, 28672, 4096)])
+                                   (2, 100, 1008), (3, 12, 131072), (1, 28672, 4096),
+                                   (48, 6912, 2560), (64, 6916, 2560)])
 def test_gate_up_relu2(env, M, N, K):
     torch, tq, oracle = env
     say(f"gate_up M={M} N={N} K={K}")
