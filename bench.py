@@ -933,7 +933,7 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
     log(f"gate_up 70b: {rows['gate_up_relu2_M1_70b_28672x8192']}")
 
     # a5: small-batch GEMM on the int8 matrix cores
-    gemm = {}
+    gemm, gate = {}, {}
     for (N, K) in workloads.GEMM_SMALL_SHAPES:
         P = pool_of(N, K, 640 << 20, 94000 + N)
         for M in workloads.GEMM_SMALL_M:
@@ -954,8 +954,31 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
                 "int8_TOPS": round(ops / us / 1e6, 2),
                 "mfma_frac": round(ops / us / 1e6 / INT8_MFMA_PEAK_TOPS, 4)}
             log(f"gemm_small M={M} {N}x{K}: {gemm[f'M{M}_{N}x{K}']}")
+        # a4 at M > 1: the gate/up pair (two matrices of this shape, the
+        # second half of the pool as the up projections) with relu^2
+        h = torch.empty(workloads.GEMM_SMALL_M[-1], N, dtype=torch.float32, device=dev)
+        half = len(P) // 2
+        for M in workloads.GEMM_SMALL_M:
+            xb = workloads.activations_bf16(M, K, seed=96 + M)
+            xt = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev).reshape(M, K)
+            q, s = tq.tq_act_quant(xt)
+            hm = h[:M]
+
+            def fg(st, P=P, q=q, s=s, hm=hm):
+                for r in range(R):
+                    i = (st + r) % half
+                    tq.tq_gate_up_relu2(P[i], 0.02, P[half + i], 0.03, q, s, hm)
+            us = loop_us(fg, half)
+            ops = 2.0 * 2 * M * N * K
+            gate[f"M{M}_{N}x{K}x2"] = {
+                "us_per_launch": round(us, 3),
+                "weight_GBs": round(2 * weight_bytes(N, K) / us / 1e3, 1),
+                "pct_hbm_peak": round(100 * 2 * weight_bytes(N, K) / us / 1e3 / HBM_PEAK_GBS, 1),
+                "int8_TOPS": round(ops / us / 1e6, 2)}
+            log(f"gate_up_relu2 M={M} {N}x{K}x2: {gate[f'M{M}_{N}x{K}x2']}")
         del P
     rows["gemm_small"] = gemm
+    rows["gate_up_relu2_small_batch"] = gate
 
     # absmean ternarizer (the step before packing), 70B-class [8192, 28672]:
     # two passes over the bf16 weights (the exact mean precedes every code)
@@ -989,8 +1012,8 @@ def measure_rows(torch, tq, workloads, timer, dev, R, per_shape):
     H, Hkv, D = 20, 5, 128
     qa = torch.randn(H, D, device=dev, dtype=torch.float32)
     oa = torch.empty(H, D, device=dev, dtype=torch.float32)
-    wsa = tq.attn_workspace(H, D, 32768, dev)
-    for L in (2048, 8192, 32768):
+    wsa = tq.attn_workspace(H, D, 131072, dev)
+    for L in (2048, 8192, 32768, 131072):
         kv_bytes = 2 * L * Hkv * D * 2
         copies = max(4, -(-(640 << 20) // kv_bytes))
         g = torch.Generator(device=dev).manual_seed(99000 + L)
