@@ -64,18 +64,13 @@ struct AttnShape {
   static_assert(NV % LPT == 0 && VPL >= 1, "butterfly shape");
   static_assert(CH >= kAttnMinChunk, "workspace sized for 64-token steps");
 };
-// Long contexts: kT = max(LPT/G, min(8, 32/G)) (at most 32 partial dots per
-// lane); short ones: at most 4 (smaller steps, so more chunks and less
-// serial work per block).
+// Tokens per lane slot and step: 4, or LPT/G where that is more (every lane
+// must end the butterfly with a complete sum).  Measured on MI355X: 8 per
+// slot at long contexts (larger steps, fewer of them) was slower with both
+// block sizes.
 template <int G, int D>
-constexpr int kt_long() {
-  return D / 8 / G > (32 / G < 8 ? 32 / G : 8) ? D / 8 / G : (32 / G < 8 ? 32 / G : 8);
-}
-template <int G, int D>
-constexpr int kt_short() {
-  return D / 8 / G > (kt_long<G, D>() < 4 ? kt_long<G, D>() : 4)
-             ? D / 8 / G
-             : (kt_long<G, D>() < 4 ? kt_long<G, D>() : 4);
+constexpr int kt_of() {
+  return D / 8 / G > 4 ? D / 8 / G : 4;
 }
 
 struct AttnArgs {
@@ -505,10 +500,12 @@ tq_status launch_attn(const float *q, const void *k, const void *v, int H,
 //  * otherwise 8-wave blocks (steps twice as long, so half as many per
 //    wave) with at most CUs / Hkv chunks per KV head, so no CU holds two
 //    blocks: L = 4096 / 8192 11.8-12.0 / 14.1 us against 13.5 / 15.7 us,
-//    L = 12288 / 32768 / 131072 15.2 / 25.4-25.6 / 72.2-72.8 us against
-//    16.3-16.4 / 28.8-29.6 / 80.0-81.2 us for 4-wave blocks with up to 64
-//    chunks (both capped: 4-wave blocks 28.0 us at 32768; uncapped 8-wave
-//    blocks 33.3 us).
+//    L = 16384 / 32768 / 131072 17.5 / 24.4-24.9 / 66.0 us against
+//    21.2 / 28.8-29.6 / 80.0-81.2 us for 4-wave blocks with up to 64 chunks
+//    (capped 4-wave blocks: 28.0 us at 32768; uncapped 8-wave blocks:
+//    33.3 us; two capped 8-wave blocks per CU: 33.2 us), at most 4 tokens
+//    per lane slot and step at every length (8 per slot beyond L = 8192:
+//    19.3-19.9 / 25.7-25.8 / 69.7-73.0 us).
 constexpr int kAttnShortL = 8192;
 constexpr int kAttnWideNW = 8;
 constexpr int kAttnScoreLds = 128 * 1024;  // bytes of scores per chunk block
@@ -517,7 +514,7 @@ template <int G, int D>
 tq_status launch_attn_g(const float *q, const void *k, const void *v, int H,
                         int Hkv, int L, float scale, float *out, float *part,
                         int num_cus, hipStream_t s) {
-  constexpr int KS = kt_short<G, D>(), KL = kt_long<G, D>();
+  constexpr int KS = kt_of<G, D>();
   if (L <= kAttnShortL) {
     constexpr int STEP = AttnShape<G, D, KS, kAttnNW>::CH;
     const int steps = (L + STEP * kAttnMaxSplits - 1) / (STEP * kAttnMaxSplits);
@@ -532,9 +529,7 @@ tq_status launch_attn_g(const float *q, const void *k, const void *v, int H,
   const int lds_min = (int)(((int64_t)L * G * 4 + kAttnScoreLds - 1) / kAttnScoreLds);
   cap = cap < lds_min ? lds_min : cap;
   cap = cap < 1 ? 1 : (cap > kAttnMaxSplits ? kAttnMaxSplits : cap);
-  if (L <= kAttnShortL)
-    return launch_attn<G, D, KS, kAttnWideNW>(q, k, v, H, Hkv, L, scale, out, part, cap, s);
-  return launch_attn<G, D, KL, kAttnWideNW>(q, k, v, H, Hkv, L, scale, out, part, cap, s);
+  return launch_attn<G, D, KS, kAttnWideNW>(q, k, v, H, Hkv, L, scale, out, part, cap, s);
 }
 
 template <int D>

@@ -63,22 +63,19 @@ def num_cus():
 
 def chunk_shape(G, D, L, Hkv, cus):
     """Tokens per lane slot over a chunk, tokens per chunk and waves per
-    block of the kernel's plan: 4-wave blocks (steps of at most 4 tokens per
-    slot, at least D/8/G; up to 64 chunks per KV head) for contexts up to
-    8192 whose chunks number at most one block per CU; otherwise 8-wave
-    blocks (at most 4 tokens per slot up to 8192, 8 beyond; at least D/8/G)
-    with at most CUs / Hkv chunks per KV head (more where a chunk's G score
+    block of the kernel's plan (steps of 4 tokens per lane slot, or D/8/G
+    where that is more): 4-wave blocks (up to 64 chunks per KV head) for
+    contexts up to 8192 whose chunks number at most one block per CU;
+    otherwise 8-wave blocks with at most CUs / Hkv chunks per KV head (more where a chunk's G score
     rows would pass 128 KiB of LDS).  Whole steps per chunk."""
     lpt = D // 8                                   # lanes per token row
     tpw = 64 // lpt                                # token slots per wave
-    kt_long = max(lpt // G, min(32 // G, 8))
-    kt_short = max(lpt // G, min(kt_long, 4))
+    kt = max(lpt // G, 4)                          # tokens per slot and step
     if L <= 8192:
-        step = 4 * tpw * kt_short
+        step = 4 * tpw * kt
         steps = -(-L // (step * 64))
         if Hkv * -(-L // (steps * step)) <= cus:
-            return steps * kt_short, steps * step, 4
-    kt = kt_short if L <= 8192 else kt_long
+            return steps * kt, steps * step, 4
     lds_min = -(-L * G * 4 // (128 * 1024))        # scores of a chunk <= 128 KiB
     cap = min(64, max(1, cus // Hkv, lds_min))
     step = 8 * tpw * kt
@@ -125,9 +122,9 @@ def check(env, L, H=20, Hkv=5, D=128, seed=0, kscale=1.0, data=None, ws=None):
 
 
 # here (256 CUs, 5 KV heads): 4-wave blocks of 64-token steps up to L = 3264
-# (one chunk up to 64 tokens, 48 chunks at 3072), then 8-wave blocks of
-# 128-token steps up to 8192 and 256-token steps beyond, at most 51 chunks
-# per KV head (131072: 32 chunks of 16 steps)
+# (one chunk up to 64 tokens, 51 chunks at 3264), then 8-wave blocks of
+# 128-token steps, at most 51 chunks per KV head (131072: 49 chunks of 21
+# steps)
 @pytest.mark.parametrize("L", [1, 7, 16, 64, 65, 100, 2048, 2049, 3264, 3265, 4096,
                                8192, 8193, 32768, 131072])
 def test_attn_2b4t_heads(env, L):
