@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
   // Dynamic LDS: scores [G][chunk], then weights; after the P.V loop the
   // per-wave outputs [NW][G][D].
   extern __shared__ float s_lds[];
-  __shared__ float red[NW][G];
+  __shared__ float red_m[NW][G], red_s[NW][G];
 
   const int chunk = a.chunk;
   const int g = blockIdx.x, c = blockIdx.y;
@@ -284,17 +284,16 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
     for (int j = 0; j < G; ++j) m[j] = wave_max_last(m[j]);
     if (lane == kWave - 1) {
 #pragma unroll
-      for (int j = 0; j < G; ++j) red[wave][j] = m[j];
+      for (int j = 0; j < G; ++j) red_m[wave][j] = m[j];
     }
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    mx[j] = red[0][j];
+    mx[j] = red_m[0][j];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mx[j] = fmaxf(mx[j], red[w][j]);
+    for (int w = 1; w < NW; ++w) mx[j] = fmaxf(mx[j], red_m[w][j]);
   }
-  __syncthreads();  // red is reused below
   {
     float sacc[G];
 #pragma unroll
@@ -310,15 +309,15 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
     for (int j = 0; j < G; ++j) sacc[j] = wave_sum_last(sacc[j]);
     if (lane == kWave - 1) {
 #pragma unroll
-      for (int j = 0; j < G; ++j) red[wave][j] = sacc[j];
+      for (int j = 0; j < G; ++j) red_s[wave][j] = sacc[j];
     }
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    sum[j] = red[0][j];
+    sum[j] = red_s[0][j];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) sum[j] += red[w][j];
+    for (int w = 1; w < NW; ++w) sum[j] += red_s[w][j];
   }
 
   // 3. unnormalized output sum_t p[t] v[t] over the chunk
