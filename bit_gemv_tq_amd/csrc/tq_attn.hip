@@ -20,7 +20,9 @@
 // LPT = D/8 consecutive lanes, 16 bytes each; a lane slot takes kT tokens per
 // step, and the next step's rows are loaded during this step's arithmetic.  The kT*G partial dots of a
 // slot are summed by a reduce-scatter butterfly over its LPT lanes.  Scores,
-// then weights, live in LDS; the first step's V rows are loaded while the
+// then weights, live in LDS token-major (the G heads of a token adjacent, so
+// the P.V loop reads them with one vector load per token); the first step's
+// V rows are loaded while the
 // softmax statistics are formed.  The chunk's max m, exp-sum l and
 // unnormalized output o go to the workspace (fp32: they are fp32 sums).  A
 // single chunk writes the output itself.
@@ -197,9 +199,9 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
   using Sh = AttnShape<G, D, KT, NW>;
   constexpr int LPT = Sh::LPT, TPW = Sh::TPW, kT = Sh::kT, STEP = Sh::CH;
   constexpr int NV = Sh::NV, VPL = Sh::VPL, NT = NW * kWave;
-  // Dynamic LDS: scores [G][chunk], then weights; after the P.V loop the
+  // Dynamic LDS: scores [chunk][G], then weights; after the P.V loop the
   // per-wave outputs [NW][G][D].
-  extern __shared__ float s_lds[];
+  extern __shared__ __align__(16) float s_lds[];
   __shared__ float red_m[NW][G], red_s[NW][G];
 
   const int chunk = a.chunk;
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
     for (int b = 0; b < VPL; ++b) {
       const int v = VPL * lt + b;
       const int i = it + (v / G) * TPW + tw;
-      if (i < n) s_lds[(v % G) * chunk + i] = val[b] * a.scale;
+      if (i < n) s_lds[i * G + v % G] = val[b] * a.scale;
     }
 #pragma unroll
     for (int u = 0; u < kT; ++u) rk[u] = rkn[u];
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
     for (int j = 0; j < G; ++j) m[j] = -INFINITY;
     for (int i = threadIdx.x; i < n; i += NT)
 #pragma unroll
-      for (int j = 0; j < G; ++j) m[j] = fmaxf(m[j], s_lds[j * chunk + i]);
+      for (int j = 0; j < G; ++j) m[j] = fmaxf(m[j], s_lds[i * G + j]);
 #pragma unroll
     for (int j = 0; j < G; ++j) m[j] = wave_max_last(m[j]);
     if (lane == kWave - 1) {
@@ -301,8 +303,8 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
     for (int i = threadIdx.x; i < n; i += NT)
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const float p = expf(s_lds[j * chunk + i] - mx[j]);
-        s_lds[j * chunk + i] = p;
+        const float p = expf(s_lds[i * G + j] - mx[j]);
+        s_lds[i * G + j] = p;
         sacc[j] += p;
       }
 #pragma unroll
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(NW *kWave) void attn_chunk_kernel(AttnArgs a) {
       widen8(r[u], x);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const float p = s_lds[j * chunk + ic] * keep;
+        const float p = s_lds[ic * G + j] * keep;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, x[e], acc[j][e]);
       }
