@@ -64,8 +64,10 @@ def num_cus():
 def chunk_shape(G, D, L, Hkv, cus):
     """Tokens per lane slot over a chunk, tokens per chunk and waves per
     block of the kernel's plan (steps of 4 tokens per lane slot, or D/8/G
-    where that is more): 4-wave blocks (up to 64 chunks per KV head) for
-    contexts up to 8192 whose chunks number at most one block per CU;
+    where that is more): one 8-wave chunk up to 256 tokens where 4-wave
+    steps would need more than one chunk; 4-wave blocks (up to 64 chunks per
+    KV head) for contexts up to 8192 whose chunks number at most one block
+    per CU;
     otherwise 8-wave blocks with at most CUs / Hkv chunks per KV head (more where a chunk's G score
     rows would pass 128 KiB of LDS).  Whole steps per chunk."""
     lpt = D // 8                                   # lanes per token row
@@ -74,7 +76,11 @@ def chunk_shape(G, D, L, Hkv, cus):
     if L <= 8192:
         step = 4 * tpw * kt
         steps = -(-L // (step * 64))
-        if Hkv * -(-L // (steps * step)) <= cus:
+        chunks = -(-L // (steps * step))
+        if chunks > 1 and L <= 256:                # one chunk of 8-wave steps
+            n8 = -(-L // (8 * tpw * kt))
+            return n8 * kt, n8 * 8 * tpw * kt, 8
+        if Hkv * chunks <= cus:
             return steps * kt, steps * step, 4
     lds_min = -(-L * G * 4 // (128 * 1024))        # scores of a chunk <= 128 KiB
     cap = min(64, max(1, cus // Hkv, lds_min))
