@@ -27,7 +27,7 @@
 // unnormalized output o go to the workspace (fp32: they are fp32 sums).  A
 // single chunk writes the output itself.
 //
-// Combine pass: block (h, slice) merges the chunks of query head h for 32
+// Combine pass: block (h, slice) merges the chunks of query head h for 16
 // dims in fp64, all of its loads issued at once (one memory round trip).
 // A second launch, not a last-arriving block: a device-wide handoff inside
 // one launch costs a store acknowledgement, an atomic and a load, about
@@ -46,7 +46,7 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnNW = kAttnThreads / kWave;
 constexpr int kAttnMinChunk = 64;    // smallest step of any (G, D, kT)
 constexpr int kAttnMaxSplits = 64;   // chunks per KV head
-constexpr int kCombineDims = 32;     // dims per combine block
+constexpr int kCombineDims = 16;     // dims per combine block
 constexpr int kCombineSubs = kAttnThreads / kCombineDims;  // row subranges
 constexpr int kCombineBatch =  // rows per thread
     (kAttnMaxSplits + kCombineSubs - 1) / kCombineSubs;
