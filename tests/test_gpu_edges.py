@@ -418,3 +418,47 @@ def test_rmsnorm_quant_gemv_closed_forms(env, K):
             y64 = oracle.rescale(acc_ref, s_w, sx, exact=True)
             err = np.abs(y.cpu().numpy().astype(np.float64) - y64[0])
             assert np.all(err <= REL_TOL * np.abs(y64[0]))
+
+
+# ------------------------------------------------ widest matrix-core plans
+def test_closed_forms_at_the_widest_quad_plans(env):
+    """The closed forms through the plans with the most quads per block: the
+    small-batch GEMM at M = 64, [2560, 6912] (3 quads per block, 16 waves)
+    and the gated pair at M = 64, [6912, 2560] (8 quads of each matrix per
+    block), where every plane scale of every quad reaches its extremes."""
+    torch, tq, oracle = env
+    M = 64
+    K, N = 6912, 2560
+    s_w = np.float32(0.023)
+    for akind in ("all127", "mixed"):
+        bits = act_rows(akind, M, K)
+        xq, xs, q_ref, s_ref = quantize(env, bits)
+        for wkind in ("plus", "minus"):
+            say(f"gemm_small widest plan M={M} K={K} N={N} W={wkind} x={akind}")
+            p, ref = packed_pair(env, weights(wkind, N, K))
+            acc = torch.full((M, N), 7, dtype=torch.int32, device="cuda")
+            y = tq.tq_gemm_small(p, s_w, xq, xs, acc=acc)
+            torch.cuda.synchronize()
+            acc_ref, y32 = oracle.gemv(ref, s_w, q_ref, s_ref, N)
+            np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+            check_closed(wkind, acc.cpu().numpy(), q_ref)
+            check_y(y.cpu().numpy(), y32, oracle.rescale(acc_ref, s_w, s_ref, exact=True))
+    K, N = 2560, 6912
+    s_g, s_u = workloads.tensor_scale(4), workloads.tensor_scale(5)
+    bits = act_rows("mixed", M, K)
+    xq, xs, q_ref, s_ref = quantize(env, bits)
+    for gk, uk in (("plus", "minus"), ("minus", "plus")):
+        say(f"gate_up widest plan M={M} K={K} N={N} gate={gk} up={uk}")
+        pg, rg = packed_pair(env, weights(gk, N, K))
+        pu, ru = packed_pair(env, weights(uk, N, K))
+        ag = torch.full((M, N), 7, dtype=torch.int32, device="cuda")
+        au = torch.full((M, N), 7, dtype=torch.int32, device="cuda")
+        h = tq.tq_gate_up_relu2(pg, s_g, pu, s_u, xq, xs, acc_gate=ag, acc_up=au)
+        torch.cuda.synchronize()
+        g_ref, u_ref, h32 = oracle.gate_up_relu2(rg, s_g, ru, s_u, q_ref, s_ref, N)
+        _, _, h64 = oracle.gate_up_relu2(rg, s_g, ru, s_u, q_ref, s_ref, N, exact=True)
+        np.testing.assert_array_equal(ag.cpu().numpy(), g_ref)
+        np.testing.assert_array_equal(au.cpu().numpy(), u_ref)
+        check_closed(gk, ag.cpu().numpy(), q_ref)
+        check_closed(uk, au.cpu().numpy(), q_ref)
+        check_y(h.cpu().numpy(), h32, h64)
