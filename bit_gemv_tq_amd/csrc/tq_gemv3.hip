@@ -13,17 +13,21 @@
 // floor(3 r_j / 256), and r_{j+1} = 3 r_j - 256 t_j.  So per row
 //   S_{4-j} = sum_k t_j(k) x_k = (3 G_j - G_{j+1}) / 256,  G_j = sum_k r_j(k) x_k,
 // six dot products that are linear in the bytes r_j and need no digit
-// extraction per weight.  The bytes r_j are formed four at a time: the even
-// and odd bytes of a dword go to the 16-bit halves of two registers, one
-// 24-bit multiply-add per register gives q*3^j + 128 in each half (no half
-// overflows: 255 * 243 + 128 < 2^16), and one byte permute gathers the low
-// bytes.  The +128 turns r_j into the signed byte r_j - 128 that
-// v_dot4_i32_i8 takes; accumulating G'_j = sum (r_j - 128) x instead of G_j
-// changes 3 G_j - G_{j+1} by 3*128 X - 128 X = 256 X (X = sum x), which is
-// exactly the code offset: 3 G'_j - G'_{j+1} = 256 * sum_k (c - 1) x_k =
-// 256 * sum_k w x.  Per dword (20 weights): 2 splits, 1 xor, 10 multiply-
-// adds, 5 permutes, 6 dot4 -- 24 VALU operations, against 21 per 64 weights
-// for the two-bit layout.
+// extraction per weight.  The bytes r_j are formed four at a time: with
+// e = d ^ 0x80808080 (each byte q ^ 128), the even and odd bytes of e go to
+// the four 16-bit fields of one 64-bit register, and one 64-bit shift-add
+// (p << 1) + p per level triples all four fields at once.  No field
+// overflows (255 * 3^5 < 2^16), and a field's low byte is q*3^j + 128 mod
+// 256, because (q ^ 128) differs from q + 128 by a multiple of 256 and
+// 128 * 3^j = 128 mod 256; one byte permute gathers the four low bytes.  The
+// +128 turns r_j into the signed byte r_j - 128 that v_dot4_i32_i8 takes
+// (e itself is that byte for j = 0); accumulating G'_j = sum (r_j - 128) x
+// instead of G_j changes 3 G_j - G_{j+1} by 3*128 X - 128 X = 256 X
+// (X = sum x), which is exactly the code offset: 3 G'_j - G'_{j+1} =
+// 256 * sum_k (c - 1) x_k = 256 * sum_k w x.  Per dword (20 weights): 1 xor,
+// 2 splits, 5 shift-adds, 5 permutes, 6 dot4 -- 19 VALU operations, against
+// 21 per 64 weights for the two-bit layout.  (The former form, two 24-bit
+// multiply-adds per level on 32-bit registers, took 24.)
 //
 // Structure as the two-bit register kernel (tq_gemv_reg.h): a team of LPR
 // lanes owns one packed row (5 output rows); lane l reads pieces l + t*LPR;
@@ -46,19 +50,28 @@ struct Gemv3Args {
   int32_t *acc;          // optional [N]
 };
 
+// 3 * p on a 64-bit register in one v_lshl_add_u64 ((p << 1) + p).  Written
+// as an asm statement because the compiler turns the plain expression into a
+// 32-bit multiply chain; pure VALU, no memory operand.
+__device__ __forceinline__ uint64_t times3(uint64_t p) {
+  uint64_t r;
+  asm("v_lshl_add_u64 %0, %1, 1, %1" : "=v"(r) : "v"(p));
+  return r;
+}
+
 // Adds the six level sums of one dword d of packed bytes against the int8
 // activations x of the same four columns.
 __device__ __forceinline__ void dot_levels(uint32_t d, int x, int (&g)[6]) {
-  g[0] = __builtin_amdgcn_sdot4((int)(d ^ 0x80808080u), x, g[0], false);
-  const uint32_t a = d & 0x00ff00ffu;                        // bytes 0, 2
-  const uint32_t b = __builtin_amdgcn_perm(0u, d, 0x0c030c01u);  // bytes 1, 3
-  uint32_t m = 1;
+  const uint32_t e = d ^ 0x80808080u;                         // q ^ 128
+  g[0] = __builtin_amdgcn_sdot4((int)e, x, g[0], false);
+  const uint32_t a = e & 0x00ff00ffu;                         // bytes 0, 2
+  const uint32_t b = __builtin_amdgcn_perm(0u, e, 0x0c030c01u);  // bytes 1, 3
+  uint64_t p = ((uint64_t)b << 32) | a;                       // fields 0 2 | 1 3
 #pragma unroll
   for (int j = 1; j < 6; ++j) {
-    m *= 3;
-    const uint32_t pa = __umul24(a, m) + 0x00800080u;
-    const uint32_t pb = __umul24(b, m) + 0x00800080u;
-    const uint32_t r = __builtin_amdgcn_perm(pb, pa, 0x06020400u);
+    p = times3(p);
+    const uint32_t r =
+        __builtin_amdgcn_perm((uint32_t)(p >> 32), (uint32_t)p, 0x06020400u);
     g[j] = __builtin_amdgcn_sdot4((int)r, x, g[j], false);
   }
 }
