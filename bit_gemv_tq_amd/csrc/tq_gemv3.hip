@@ -202,12 +202,13 @@ struct Plan3 {
 // for 256-thread blocks, lowered at launch to what the compiled kernel lets
 // a CU hold (this VALU-heavy decode gains from more waves per SIMD:
 // measured on MI355X, [28672,8192] 14.0 against 14.6 us with 3 per CU,
-// [57344,4096] 14.4 against 15.2 us), and 4 for 512-thread blocks.  At
-// 5-8 pieces per lane a CU holds only 2 of the 512-thread blocks (86-114
-// VGPRs), so a grid of one row per team beyond that runs as a second wave
-// of blocks; measured on MI355X it still beat a grid of 2 blocks per CU
-// whose teams walk two rows (15.9 against 16.8 us at [8192,28672]: 820
-// blocks of one row per team), so those grids are not lowered.
+// [57344,4096] 14.4 against 15.2 us), and 4 for 512-thread blocks.  A CU
+// holds 3 of the 512-thread blocks at 7 pieces per lane (76 VGPRs) and 2 at
+// 8 (96), so a grid of one row per team beyond that runs as a second,
+// partial wave of blocks; measured on MI355X it still beat a grid of 2
+// blocks per CU whose teams walk two rows (15.9 against 16.8 us at
+// [8192,28672] with the former 24-operation decode: 820 blocks of one row
+// per team), so those grids are not lowered.
 Plan3 plan3(int64_t n5, int64_t kp, int num_cus) {
   Plan3 pl{};
   int lpr = 16;
